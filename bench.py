@@ -1,0 +1,289 @@
+"""Benchmark of the routed-expert MoE FFN on one MI355X.
+
+Default workload: the Qwen3-style decode layer (hidden 2048, expert
+intermediate 768, 128 experts, top-8, MXFP8 weights, BF16 activations) at
+B = 32 tokens, run by moe_layer's path for that batch (the output-centric
+decode kernels).  One step = one layer call over one batch; consecutive steps
+cycle through several independent copies of the layer's weights with their
+own routing draws (as the layers of a model do), so every step streams its
+experts from HBM rather than from a cache warmed by the previous step.
+
+Prints ONE JSON line: value = achieved HBM bandwidth in TB/s counted from the
+algorithmic bytes of each step's actual routing (each touched expert's weights
+and scales once, plus x, ids, routing weights and y), ms_per_step = time per
+layer.  Also: the measured copy-kernel peak and the fraction of it, a batch
+sweep, the dominant kernel's roofline entry, and the float64 oracle timed on
+the host cores (CPU baseline leg).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+DOMINANT = "gate_up_decode_kernel"
+KERNEL_SOURCES = ["mixture_experts_decode_amd/csrc/decode.hip",
+                  "mixture_experts_decode_amd/csrc/device.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--batch", type=int, default=32)
+    p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
+    p.add_argument("--block", type=int, default=64)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-copy-peak", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg_name, batch):
+    """HBM traffic per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{DOMINANT}_{cfg_name}_b{batch}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import mixture_experts_decode_amd as moe
+
+    moe.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIGS[args.config]
+    B = args.batch
+    stream = torch.cuda.current_stream()
+
+    # ---- weights: one generated layer, copied so steps rotate through
+    # independent memory (>= ~2.5 GB in total)
+    arrays = W.all_experts(cfg)
+    w0 = moe.Weights.from_arrays(cfg, arrays)
+    layer_bytes = w0.nbytes()
+    n_layers = max(2, min(16, math.ceil(2.5e9 / layer_bytes)))
+    layers = [w0]
+    for _ in range(n_layers - 1):
+        t = [None if a is None else a.clone() for a in w0.tensors]
+        layers.append(moe.Weights(cfg.fmt, cfg.hidden, cfg.inter, cfg.num_experts,
+                                  cfg.num_shared, *t))
+    ebytes = W.expert_bytes(cfg)
+    act_bytes = 2 if cfg.act == "bf16" else 4
+
+    def make_inputs(b, variant):
+        x = W.activations(cfg, b, variant)
+        ids, wts = W.routing(cfg, b, variant=variant)
+        xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
+              else torch.from_numpy(x)).to(dev)
+        u = len(W.touched_experts(cfg, ids))
+        io = b * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes + b * cfg.hidden * 4
+        gate_up_bytes = u * (ebytes - ebytes_down(cfg)) + b * cfg.hidden * act_bytes + ids.nbytes \
+            + b * (cfg.top_k + cfg.num_shared) * cfg.inter * 4
+        return dict(x=xd, ids=torch.from_numpy(ids).to(dev), wts=torch.from_numpy(wts).to(dev),
+                    bytes=u * ebytes + io, gate_up_bytes=gate_up_bytes, U=u)
+
+    def ebytes_down(c):
+        shapes = W.weight_shapes(c)
+        tot = 0
+        for k in ("w2", "w2_scale"):
+            if k in shapes:
+                s, d = shapes[k]
+                tot += int(np.prod(s[1:])) * np.dtype(d).itemsize
+        return tot
+
+    # ---- copy peak (read + write bytes), best of 20, 2 GiB each way
+    copy_peak = read_peak = None
+    if not args.no_copy_peak:
+        n = 2 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        moe.util_fill(src, n, 0x3c3c3c3c)
+        sink = torch.zeros(4096, dtype=torch.float32, device=dev)
+        best_c = best_r = 1e30
+        for _ in range(20):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            moe.util_copy(src, dst, n)
+            e1.record(stream)
+            moe.util_read(src, n, sink)
+            e2.record(stream)
+            e2.synchronize()
+            best_c = min(best_c, e0.elapsed_time(e1))
+            best_r = min(best_r, e1.elapsed_time(e2))
+        copy_peak = 2 * n / (best_c * 1e-3) / 1e12
+        read_peak = n / (best_r * 1e-3) / 1e12
+        del src, dst
+
+    def run_steps(b, steps, warmup, path):
+        ins = [make_inputs(b, v) for v in range(n_layers)]
+        need = moe.layer_workspace_bytes(layers[0], b, cfg.top_k, path, args.block)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        y = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
+        chosen = moe.choose_path(layers[0], b, cfg.top_k) if path == "auto" else path
+        h = torch.empty((b, cfg.top_k + cfg.num_shared, cfg.inter), dtype=torch.float32,
+                        device=dev)
+
+        def step(i, ev=None):
+            L = layers[i % n_layers]
+            d = ins[i % n_layers]
+            if chosen == "decode":
+                if ev is not None:
+                    ev[0].record(stream)
+                moe.gate_up(L, d["x"], d["ids"], h=h)
+                if ev is not None:
+                    ev[1].record(stream)
+                moe.down(L, h, d["ids"], d["wts"], y=y)
+                if ev is not None:
+                    ev[2].record(stream)
+            else:
+                moe.layer(L, d["x"], d["ids"], d["wts"], path="grouped", block=args.block, y=y,
+                          workspace=ws)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for i in range(steps):
+            step(i, evs[i] if chosen == "decode" else None)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = s0.elapsed_time(s1)
+        tot_bytes = sum(ins[i % n_layers]["bytes"] for i in range(steps))
+        res = {"B": b, "path": chosen, "us_per_layer": total_ms * 1e3 / steps,
+               "TBps": tot_bytes / (total_ms * 1e-3) / 1e12,
+               "U_mean": float(np.mean([d["U"] for d in ins])), "wall_s": wall}
+        if chosen == "decode":
+            gu = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+            dn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(steps)]
+            gub = sum(ins[i % n_layers]["gate_up_bytes"] for i in range(steps))
+            res["gate_up_us"] = float(np.mean(gu)) * 1e3
+            res["down_us"] = float(np.mean(dn)) * 1e3
+            res["gate_up_GBps"] = gub / (sum(gu) * 1e-3) / 1e9
+            res["gate_up_bytes_per_launch"] = gub / steps
+        return res
+
+    main_res = run_steps(B, args.steps, args.warmup, args.path)
+
+    sweep = []
+    if not args.no_sweep and args.config == 2:
+        for b in cfg.batches:
+            r = run_steps(b, 50, 5, args.path)
+            sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
+                          if k in ("B", "path", "us_per_layer", "TBps", "U_mean", "gate_up_us",
+                                   "down_us")})
+
+    roofline = None
+    if main_res["path"] == "decode":
+        achieved = main_res["gate_up_GBps"]
+        traffic = load_traffic(cfg.name, B)
+        roofline = {"kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic,
+                    "algorithmic_bytes_per_launch": round(main_res["gate_up_bytes_per_launch"]),
+                    "avg_launch_us": round(main_res["gate_up_us"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, B, arrays)
+
+    value = main_res["TBps"]
+    out = {
+        "metric": "us per MoE layer & achieved HBM TB/s (fraction of peak), 1 GPU",
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["us_per_layer"] / 1e3, 5),
+        "us_per_layer": round(main_res["us_per_layer"], 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-weights/bf16-act/f32-acc" if cfg.fmt == "mxfp8" else cfg.fmt,
+        "data": "synthetic (seeded; random-init weights of the named shape)",
+        "config": {"workload": cfg.name, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "experts": cfg.num_experts, "top_k": cfg.top_k, "batch": B,
+                   "weight_format": cfg.fmt, "path": main_res["path"],
+                   "layers_rotated": n_layers, "touched_experts_mean": main_res["U_mean"]},
+        "copy_peak_TBps": None if copy_peak is None else round(copy_peak, 3),
+        "read_peak_TBps": None if read_peak is None else round(read_peak, 3),
+        "frac_of_copy_peak": None if copy_peak is None else round(value / copy_peak, 4),
+        "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
+        "kernels_us": {k: round(main_res[k], 2) for k in ("gate_up_us", "down_us") if k in main_res},
+        "sweep": sweep,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, B, arrays):
+    """The float64 oracle timed on this host's cores on one full layer call of
+    the same workload (B tokens, its first routing draw)."""
+    import workloads as W
+    from oracle import layer as L
+    x = W.activations(cfg, B, 0)
+    ids, wts = W.routing(cfg, B, variant=0)
+
+    def get(e):
+        return {k: (None if v is None else v[e]) for k, v in arrays.items()}
+
+    kw = dict(fmt=cfg.fmt, num_experts=cfg.num_experts, num_shared=cfg.num_shared, get_expert=get)
+    t0 = time.perf_counter()
+    L.moe_layer(L.activations_f64(x, cfg.act), ids, wts, **kw)
+    dt = time.perf_counter() - t0
+    u = len(W.touched_experts(cfg, ids))
+    act_bytes = 2 if cfg.act == "bf16" else 4
+    nbytes = u * W.expert_bytes(cfg) + B * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes \
+        + B * cfg.hidden * 4
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": round(nbytes / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "us_per_layer": round(dt * 1e6, 1),
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"one full layer call of {cfg.name}, B={B} ({u} touched experts), float64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,285 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed-expert MoE FFN library for MI355X (gfx950).
+ *
+ * One MoE layer's routed experts compute, for every token t routed to the k
+ * experts e_tj with weights w_tj,
+ *
+ *     y_t = sum_j w_tj * Wd[e_tj] ( SiLU(Wg[e_tj] x_t) * Wu[e_tj] x_t )
+ *
+ * (SwiGLU experts and the weighted top-k combine: warp-decode post, sections on
+ * the traditional MoE path and on how the two kernels work).  Two regimes:
+ *
+ *  - decode (output-centric, small batches): moe_gate_up + moe_down.  Every
+ *    output scalar is produced by exactly one 64-lane wavefront that streams
+ *    the expert weight rows it needs, converts the stored format in registers
+ *    and keeps FP32 accumulators (warp-decode post: the two kernels, warp
+ *    independence);
+ *  - grouped (expert-centric, large batches): moe_align_sort, then
+ *    moe_gather_quant, moe_grouped_gate_up, moe_grouped_down, moe_combine on
+ *    gfx950 block-scaled matrix cores (align-and-sort article: background,
+ *    D-C-P algorithm, CK fused-MoE section on online FP8 quantisation).
+ *
+ * moe_layer runs either regime, or picks one (moe_choose_path).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device memory must be device memory of the current
+ *    HIP device; the caller owns all of it.  The library never allocates,
+ *    frees or synchronises; every call enqueues kernels on `stream` (a
+ *    hipStream_t passed as void*, NULL = the default stream) and returns.
+ *  - Every shape / pointer / enum problem is detected on the host before any
+ *    launch and returns an error with nothing enqueued.  A launch failure
+ *    reported by the HIP runtime returns MOE_ERR_HIP.  No exceptions, no exit.
+ *  - Preconditions NOT checked (they would need a device read): expert ids in
+ *    [0, num_experts); finite weights and scales; outputs not aliasing inputs.
+ *  - The library keeps no mutable global state apart from a per-device cache
+ *    of the compute-unit count; calls are thread-safe.  Calls may be captured
+ *    in a HIP graph: they record kernels only.
+ *
+ * Weight storage (per expert e in [0, E+S), S = num_shared in {0, 1}; the
+ * shared expert is stored as index E):
+ *   w13 [E+S][2][I][H*]  gate rows (index 0) then up rows (index 1), [out][in]
+ *   w2  [E+S][H][I*]     down rows, [out][in]
+ *   MOE_W_F32        : float32 values, no scales.
+ *   MOE_W_MXFP8      : E4M3FN bytes; scales E8M0 bytes, one per 32 consecutive
+ *                      input elements: w13_scale [E+S][2][I][H/32],
+ *                      w2_scale [E+S][H][I/32].
+ *   MOE_W_MXFP4      : E2M1 nibbles, two per byte, even element in the low
+ *                      nibble (rows are H/2 resp. I/2 bytes); E8M0 scales as MXFP8.
+ *   MOE_W_FP8_BLK128 : E4M3FN bytes; float32 scale per 128x128 tile of each
+ *                      [out][in] matrix: w13_scale [E+S][2][I/128][H/128],
+ *                      w2_scale [E+S][H/128][I/128].
+ * Routing: topk_ids [T][k] int32 and topk_weights [T][k] float32 list the
+ * routed slots; with S = 1 every token also runs slot k on expert E with
+ * weight 1.0.  "slots" below means k + S.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,        /* bad pointer, size or enum value          */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid but not implemented combination    */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* the HIP runtime reported an error        */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_W_F32 = 0,
+  MOE_W_MXFP8 = 1,
+  MOE_W_MXFP4 = 2,
+  MOE_W_FP8_BLK128 = 3
+} moe_weight_format;
+
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 } moe_path;
+
+/* One layer's expert weights.  A host struct holding device pointers. */
+typedef struct {
+  int32_t hidden;        /* H                                              */
+  int32_t inter;         /* I                                              */
+  int32_t num_experts;   /* E, routed experts                              */
+  int32_t num_shared;    /* S in {0, 1}; the shared expert is index E      */
+  int32_t format;        /* moe_weight_format                              */
+  const void* w13;       /* device, layout above                           */
+  const void* w13_scale; /* device, NULL for MOE_W_F32                     */
+  const void* w2;        /* device                                         */
+  const void* w2_scale;  /* device, NULL for MOE_W_F32                     */
+} moe_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* ABI version of this header (incremented on incompatible change). */
+int32_t moe_abi_version(void);
+
+/* ------------------------------------------------------------------ */
+/* Decode regime (output-centric).                                     */
+/* ------------------------------------------------------------------ */
+
+/* Largest T * slots the decode kernels accept (the routed ids of one call
+ * are staged on chip). */
+int32_t moe_decode_max_entries(void);
+
+/*
+ * moe_gate_up: h[t][j][n] = SiLU(g) * u with g = Wg[e_tj][n,:] . x_t and
+ * u = Wu[e_tj][n,:] . x_t, for every token t < T, slot j < slots, neuron n < I
+ * (warp-decode post, section on how the two kernels work: one wavefront per
+ * intermediate neuron of a (token, routed expert) pair, gate and up rows
+ * streamed with the activation read once for both, SiLU(gate) * up applied
+ * after the wave reduction).  A wavefront owns neuron rows of one expert and
+ * produces those neurons for every slot routed to that expert in the batch, so
+ * each weight row is read once per call; every h scalar is written exactly
+ * once and its reduction order does not depend on the batch.
+ *   x        device, [T][H], x_dtype (MOE_DT_F32 only with MOE_W_F32 weights)
+ *   topk_ids device, [T][k] int32
+ *   h        device, [T][slots][I], h_dtype
+ * T == 0 is a no-op.  T * slots must not exceed moe_decode_max_entries().
+ */
+moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
+                       const int32_t* topk_ids, int32_t T, int32_t k,
+                       void* h, int32_t h_dtype, void* stream);
+
+/*
+ * moe_down: y[t][d] = sum_j w_tj * (Wd[e_tj][d,:] . h[t][j][:]) for every
+ * token t < T and output d < H (warp-decode post, section on how the two
+ * kernels work: one wavefront per output dimension of a token walks all of
+ * the token's experts, folds each routing weight into one FP32 accumulator and
+ * finishes with a butterfly reduction; the combine is part of the projection).
+ * The slots are summed into per-lane accumulators in slot order; y has no
+ * intermediate buffer.
+ *   h            device, [T][slots][I], h_dtype
+ *   topk_ids     device, [T][k] int32; topk_weights device, [T][k] float32
+ *   y            device, [T][H], y_dtype
+ */
+moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
+                    const int32_t* topk_ids, const float* topk_weights,
+                    int32_t T, int32_t k, void* y, int32_t y_dtype, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Align-and-sort (expert-centric front end).                          */
+/* ------------------------------------------------------------------ */
+
+/* Padded capacity: n + (E+S)*(BS-1) with n = T*(k+S). */
+size_t moe_align_sort_capacity(int32_t T, int32_t k, int32_t num_experts,
+                               int32_t num_shared, int32_t block_size);
+
+/* Bytes of device scratch moe_align_sort needs. */
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t num_experts,
+                                      int32_t num_shared, int32_t block_size);
+
+/*
+ * moe_align_sort: groups the n = T*(k+S) (token, slot) entries by expert and
+ * pads every expert's run to a multiple of block_size (align-and-sort article:
+ * background -- sort by expert id, align to the grouped GEMM's block;
+ * D-C-P section -- distributed counting, cumulative sum of the aligned counts,
+ * parallel placement).  Entry i = t*(k+S) + j; with S = 1 the entry of slot k
+ * is expert E.  Results (bit-exact, deterministic):
+ *   expert_offsets[e]   exclusive prefix of the padded counts, e in [0, E+S]
+ *   *num_tokens_post_padded = expert_offsets[E+S]  (device scalar)
+ *   sorted_token_ids[expert_offsets[e] + r] = r-th smallest entry of expert e
+ *                          (ascending, i.e. stable); the padding tail of each
+ *                          run holds the sentinel n
+ *   expert_ids[b]       expert of block b, b < num_tokens_post_padded/block_size
+ * Only the first num_tokens_post_padded entries of sorted_token_ids and the
+ * first num_tokens_post_padded/block_size of expert_ids are written.
+ *   topk_ids          device [T][k] int32
+ *   sorted_token_ids  device [capacity] int32
+ *   expert_ids        device [capacity / block_size] int32
+ *   expert_offsets    device [E+S+1] int32
+ *   num_tokens_post_padded device [1] int32
+ *   workspace         device, >= moe_align_sort_workspace_bytes(...)
+ * block_size must be 1..1024; E+S must be 1..1024.
+ */
+moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k,
+                          int32_t num_experts, int32_t num_shared, int32_t block_size,
+                          int32_t* sorted_token_ids, int32_t* expert_ids,
+                          int32_t* expert_offsets, int32_t* num_tokens_post_padded,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* Grouped regime steps (expert-centric, block-scaled MFMA).           */
+/* ------------------------------------------------------------------ */
+
+/*
+ * moe_gather_quant: for every sorted row r < *num_tokens_post_padded, reads
+ * x row t = sorted_token_ids[r] / slots (zeros for a sentinel row) and
+ * MX-quantises it per 32 consecutive elements: shared exponent
+ * floor(log2 amax) - 8 (clamped to [-127, 127], -127 for a zero block), scale
+ * byte = exponent + 127, elements divided by 2^exponent, saturated to +-448
+ * and rounded to the nearest E4M3 value, ties to even (align-and-sort article,
+ * CK section: online FP8 quantisation of tokens ahead of the grouped GEMM;
+ * warp-decode post, buffer section: the expert-major activation copy).
+ *   x    device [T][H], x_dtype (BF16 or F32)
+ *   xq   device [capacity][H] E4M3 bytes;  xs device [capacity][H/32] E8M0
+ * H must be a multiple of 32.
+ */
+moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                            int32_t slots, const int32_t* sorted_token_ids,
+                            const int32_t* num_tokens_post_padded, int32_t capacity,
+                            uint8_t* xq, uint8_t* xs, void* stream);
+
+/*
+ * moe_grouped_gate_up: for every block b < *num_tokens_post_padded/block_size
+ * with expert e = expert_ids[b], G = Xq[b] Wg[e]^T and U = Xq[b] Wu[e]^T on
+ * block-scaled MFMA with FP32 accumulation, then h = SiLU(G) * U quantised
+ * to MXFP8 per 32 consecutive neurons (the same rule as moe_gather_quant)
+ * (GC-MoE abstract: grouped GEMM with SwiGLU and requantisation fused in the
+ * epilogue).
+ *   xq/xs   device, from moe_gather_quant
+ *   hq      device [capacity][I] E4M3;  hs device [capacity][I/32] E8M0
+ * Weight formats: MOE_W_MXFP8, MOE_W_MXFP4, MOE_W_FP8_BLK128.
+ * block_size in {32, 64, 128}; H multiple of 128; I multiple of 64.
+ */
+moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const uint8_t* xs,
+                               const int32_t* expert_ids,
+                               const int32_t* num_tokens_post_padded, int32_t capacity,
+                               int32_t block_size, uint8_t* hq, uint8_t* hs, void* stream);
+
+/*
+ * moe_grouped_down: for every block b with expert e, O = Hq[b] Wd[e]^T on
+ * block-scaled MFMA; row r of O is multiplied by the routing weight of entry
+ * i = sorted_token_ids[r] (1.0 for the shared slot) and stored to
+ * slot_out[i][:]; sentinel rows are dropped (warp-decode post, buffer
+ * section: the per-expert output buffer of the expert-centric path).
+ *   slot_out device [T*slots][H] float32
+ */
+moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8_t* hs,
+                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                            const int32_t* num_tokens_post_padded, int32_t capacity,
+                            int32_t block_size, const float* topk_weights, int32_t T,
+                            int32_t k, float* slot_out, void* stream);
+
+/*
+ * moe_combine: y[t][d] = sum_{j < slots} slot_out[t*slots + j][d], summed in
+ * slot order (deterministic; warp-decode post, traditional path: the final
+ * combine of per-expert outputs).
+ *   y device [T][H], y_dtype
+ */
+moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t H,
+                       void* y, int32_t y_dtype, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* The whole layer.                                                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * moe_choose_path: the regime moe_layer(MOE_PATH_AUTO) runs for T tokens
+ * (warp-decode post, last section: output-centric decode wins while the work
+ * each expert shares is small; prefill and large batches favour expert-centric
+ * packing).  Returns MOE_PATH_DECODE or MOE_PATH_GROUPED.
+ */
+int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k);
+
+/* Workspace bytes moe_layer needs for this path (AUTO resolved as above). */
+size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k,
+                                 int32_t path, int32_t block_size);
+
+/*
+ * moe_layer: y = the routed-expert FFN of the layer for T tokens.
+ *   path        MOE_PATH_AUTO / DECODE / GROUPED
+ *   block_size  grouped path M block (32, 64 or 128); ignored for decode
+ *   chosen      host, nullable: receives the path that ran
+ *   workspace   device, >= moe_layer_workspace_bytes(W, T, k, path, block_size)
+ * The decode path keeps activations exact (BF16/FP32 in, FP32 accumulate);
+ * the grouped path quantises x and h to MXFP8 for the matrix cores.
+ */
+moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
+                     const int32_t* topk_ids, const float* topk_weights,
+                     int32_t T, int32_t k, void* y, int32_t y_dtype,
+                     int32_t path, int32_t block_size,
+                     void* workspace, size_t workspace_bytes,
+                     int32_t* chosen, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

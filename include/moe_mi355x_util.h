@@ -1,0 +1,42 @@
+/*
+ * moe_mi355x_util.h -- measurement kernels exported by the same library.
+ *
+ * The denominators of the bandwidth figures are measured, not assumed: the
+ * warp-decode post (hardware-efficiency section) rates its decode against a
+ * copy kernel reading contiguous memory on the same GPU, and so do we.
+ * Conventions as in moe_mi355x.h (device pointers, async on `stream`).
+ */
+#ifndef MOE_MI355X_UTIL_H
+#define MOE_MI355X_UTIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dst[0:bytes) = src[0:bytes) with 16-byte non-temporal loads and stores,
+ * grid sized to fill every compute unit.  bytes must be a multiple of 16 and
+ * both pointers 16-byte aligned. */
+moe_status moe_util_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Reads src[0:bytes) (16-byte non-temporal loads) and writes one float per
+ * workgroup to sink[0:moe_util_read_sink_len()) so the loads are live. */
+moe_status moe_util_read(const void* src, size_t bytes, float* sink, void* stream);
+int32_t moe_util_read_sink_len(void);
+
+/* Writes `value` to every 32-bit word of dst[0:bytes): evicts caches between
+ * timed calls.  bytes must be a multiple of 16. */
+moe_status moe_util_fill(void* dst, size_t bytes, uint32_t value, void* stream);
+
+/* Compute units of the current device (cached). */
+int32_t moe_util_num_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_UTIL_H */

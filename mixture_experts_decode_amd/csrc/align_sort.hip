@@ -1,0 +1,260 @@
+// MoE align-and-sort: group (token, slot) entries by expert, pad every
+// expert's run to the grouped GEMM's block size.
+//
+// Structure after the align-and-sort article's D-C-P section (distributed
+// concurrent counting, then the cumulative sums -- local unaligned, merged,
+// aligned global, stored -- then parallel placement), re-planned for gfx950:
+//  * count: every wavefront histograms its own contiguous range of entries in
+//    a private LDS slice and stores the slice (no atomics to global memory,
+//    no zero-initialised buffers, so the call is graph-capturable);
+//  * prefix: one workgroup merges the per-wave histograms per expert into
+//    exclusive per-wave bases, aligns each expert's total to the block size,
+//    scans over experts, and writes offsets, block expert ids and the
+//    sentinel padding;
+//  * place: every wavefront walks its range again in order and gives each
+//    entry its stable rank among equal ids (a match mask from per-bit
+//    ballots, then a popcount), so the output is deterministic and ordered by
+//    entry index inside every expert's run.
+// Cross-workgroup data goes through L2 between launches (gfx950 has no
+// on-chip workgroup-to-workgroup exchange; the article's CK/AITER section
+// notes the same of CDNA3).
+
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kAsBlock = 256;
+constexpr int kAsWaves = kAsBlock / kWave;
+constexpr int kMaxWaves = 128;        // count/place wavefronts per call
+constexpr int kPrefixBlock = 1024;
+
+struct AsArgs {
+  const int32_t* ids;
+  int T, k, slots, E, n_exp, bs, n;   // n = T*slots entries, n_exp = E + S
+  int per_wave;                        // entries per wavefront (multiple of 64)
+  int n_waves;
+  int id_bits;                         // bits to tell experts apart
+  int32_t* hist;                       // [n_waves][n_exp]
+  int32_t* base;                       // [n_waves][n_exp]
+  int32_t* sorted;
+  int32_t* expert_ids;
+  int32_t* offsets;
+  int32_t* npp;
+};
+
+__device__ __forceinline__ int entry_expert(const AsArgs& a, int i) {
+  int e;
+  if (a.slots == a.k) {
+    e = a.ids[i];
+  } else {
+    const int t = i / a.slots, j = i - t * a.slots;
+    e = j < a.k ? a.ids[t * a.k + j] : a.E;
+  }
+  return (unsigned)e < (unsigned)a.n_exp ? e : 0;
+}
+
+__global__ __launch_bounds__(kAsBlock) void as_count_kernel(const AsArgs a) {
+  __shared__ int s_hist[kAsWaves][kMaxExpertsTotal];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wl = threadIdx.x >> 6;
+  const int w = blockIdx.x * kAsWaves + wl;
+  if (w >= a.n_waves) return;
+  int* h = s_hist[wl];
+  for (int e = lane; e < a.n_exp; e += kWave) h[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int lo = w * a.per_wave;
+  const int hi = min(lo + a.per_wave, a.n);
+  for (int i = lo + lane; i < hi; i += kWave) atomicAdd(&h[entry_expert(a, i)], 1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int32_t* out = a.hist + (size_t)w * a.n_exp;
+  for (int e = lane; e < a.n_exp; e += kWave) out[e] = h[e];
+}
+
+// One workgroup: per-expert merge over waves, alignment, expert scan.
+__global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a) {
+  __shared__ int s_part[kPrefixBlock];
+  __shared__ int s_off[kMaxExpertsTotal + 1];
+  __shared__ int s_cnt[kMaxExpertsTotal];
+  __shared__ int s_scan[kPrefixBlock];
+  const int tid = threadIdx.x;
+  // G threads per expert, each over a contiguous run of waves
+  const int G = max(1, min(kPrefixBlock / a.n_exp, 8));
+  const int per = (a.n_waves + G - 1) / G;
+
+  for (int base_e = 0; base_e < a.n_exp; base_e += kPrefixBlock / G) {
+    const int e = base_e + tid / G;
+    const int g = tid % G;
+    const bool act = tid / G < kPrefixBlock / G && e < a.n_exp;
+    const int w0 = g * per, w1 = min(w0 + per, a.n_waves);
+    int sum = 0;
+    if (act)
+      for (int w = w0; w < w1; ++w) sum += a.hist[(size_t)w * a.n_exp + e];
+    s_part[tid] = sum;
+    __syncthreads();
+    if (act) {
+      int pre = 0, tot = 0;
+      for (int q = 0; q < G; ++q) {
+        const int v = s_part[(tid / G) * G + q];
+        if (q < g) pre += v;
+        tot += v;
+      }
+      if (g == 0) s_cnt[e] = tot;
+      // exclusive base of each wave within the expert (offset added later)
+      int run = pre;
+      for (int w = w0; w < w1; ++w) {
+        const int c = a.hist[(size_t)w * a.n_exp + e];
+        a.base[(size_t)w * a.n_exp + e] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+
+  // padded counts, exclusive scan over experts (blocked: thread handles a run)
+  const int per_t = (a.n_exp + kPrefixBlock - 1) / kPrefixBlock;
+  const int e0 = tid * per_t, e1 = min(e0 + per_t, a.n_exp);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += (s_cnt[e] + a.bs - 1) / a.bs * a.bs;
+  s_scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kPrefixBlock; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int run = s_scan[tid] - local;
+  for (int e = e0; e < e1; ++e) {
+    s_off[e] = run;
+    run += (s_cnt[e] + a.bs - 1) / a.bs * a.bs;
+  }
+  if (tid == kPrefixBlock - 1) s_off[a.n_exp] = s_scan[tid];
+  __syncthreads();
+  const int total = s_off[a.n_exp];
+  for (int e = tid; e <= a.n_exp; e += kPrefixBlock) a.offsets[e] = s_off[e];
+  if (tid == 0) *a.npp = total;
+
+  // block -> expert (binary search over the offsets)
+  const int n_blocks = total / a.bs;
+  for (int b = tid; b < n_blocks; b += kPrefixBlock) {
+    const int pos = b * a.bs;
+    int lo = 0, hi = a.n_exp - 1;          // last e with s_off[e] <= pos
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
+    }
+    a.expert_ids[b] = lo;
+  }
+  // sentinel tails: (expert, r) pairs with r < bs - 1
+  const int padw = a.bs - 1;
+  if (padw > 0) {
+    for (int q = tid; q < a.n_exp * padw; q += kPrefixBlock) {
+      const int e = q / padw, r = q - e * padw;
+      const int c = s_cnt[e];
+      const int p = (c + a.bs - 1) / a.bs * a.bs;
+      if (c + r < p) a.sorted[s_off[e] + c + r] = a.n;
+    }
+  }
+  // per-wave bases become absolute
+  for (int q = tid; q < a.n_waves * a.n_exp; q += kPrefixBlock) {
+    const int e = q % a.n_exp;
+    a.base[q] += s_off[e];
+  }
+}
+
+__global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
+  __shared__ int s_ctr[kAsWaves][kMaxExpertsTotal];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wl = threadIdx.x >> 6;
+  const int w = blockIdx.x * kAsWaves + wl;
+  if (w >= a.n_waves) return;
+  int* ctr = s_ctr[wl];
+  const int32_t* bse = a.base + (size_t)w * a.n_exp;
+  for (int e = lane; e < a.n_exp; e += kWave) ctr[e] = bse[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int lo = w * a.per_wave;
+  const int hi = min(lo + a.per_wave, a.n);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int i0 = lo; i0 < hi; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool valid = i < hi;
+    const int e = valid ? entry_expert(a, i) : 0;
+    unsigned long long peers = __ballot(valid);
+    for (int b = 0; b < a.id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    const int cnt = __popcll(peers);
+    int dst = 0;
+    if (valid) dst = ctr[e] + rank;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      a.sorted[dst] = i;
+      if (rank == cnt - 1) ctr[e] = dst + 1;     // last of its group advances the counter
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+AsArgs make_args(const int32_t* ids, int T, int k, int E, int S, int bs) {
+  AsArgs a{};
+  a.ids = ids;
+  a.T = T;
+  a.k = k;
+  a.slots = k + S;
+  a.E = E;
+  a.n_exp = E + S;
+  a.bs = bs;
+  a.n = T * a.slots;
+  const int chunks = (a.n + kWave - 1) / kWave;
+  const int per_chunks = std::max(1, (chunks + kMaxWaves - 1) / kMaxWaves);
+  a.per_wave = per_chunks * kWave;
+  a.n_waves = std::max(1, (a.n + a.per_wave - 1) / a.per_wave);
+  int bits = 0;
+  while ((1 << bits) < a.n_exp) ++bits;
+  a.id_bits = bits;
+  return a;
+}
+
+}  // namespace
+
+size_t align_sort_workspace_bytes(int n_entries, int n_experts) {
+  const int chunks = (n_entries + kWave - 1) / kWave;
+  const int per_chunks = std::max(1, (chunks + kMaxWaves - 1) / kMaxWaves);
+  const int per_wave = per_chunks * kWave;
+  const int n_waves = std::max(1, (n_entries + per_wave - 1) / per_wave);
+  return (size_t)2 * n_waves * n_experts * sizeof(int32_t);
+}
+
+hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int bs,
+                             int32_t* sorted, int32_t* expert_ids, int32_t* offsets,
+                             int32_t* npp, void* ws, hipStream_t s) {
+  AsArgs a = make_args(ids, T, k, E, S, bs);
+  a.hist = reinterpret_cast<int32_t*>(ws);
+  a.base = a.hist + (size_t)a.n_waves * a.n_exp;
+  a.sorted = sorted;
+  a.expert_ids = expert_ids;
+  a.offsets = offsets;
+  a.npp = npp;
+  const int blocks = (a.n_waves + kAsWaves - 1) / kAsWaves;
+  hipLaunchKernelGGL(as_count_kernel, dim3(blocks), dim3(kAsBlock), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(as_prefix_kernel, dim3(1), dim3(kPrefixBlock), 0, s, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(as_place_kernel, dim3(blocks), dim3(kAsBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,352 @@
+// C ABI layer: argument validation (host only, before any launch), workspace
+// sizing, regime choice, and dispatch to the kernel translation units.
+
+#include <stdint.h>
+
+#include "internal.h"
+#include "moe_mi355x.h"
+#include "moe_mi355x_util.h"
+
+namespace {
+
+using moe::kDecodeMaxEntries;
+using moe::kMaxExpertsTotal;
+
+constexpr int32_t kAbiVersion = 1;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+moe_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+  return MOE_ERR_HIP;
+}
+
+bool dtype_ok(int32_t d) { return d == MOE_DT_F32 || d == MOE_DT_BF16; }
+
+moe_status check_weights(const moe_weights* W) {
+  if (!W) return MOE_ERR_INVALID_ARG;
+  if (W->hidden <= 0 || W->inter <= 0 || W->num_experts <= 0) return MOE_ERR_INVALID_ARG;
+  if (W->num_shared != 0 && W->num_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (W->num_experts + W->num_shared > kMaxExpertsTotal) return MOE_ERR_UNSUPPORTED;
+  if (!W->w13 || !W->w2 || !aligned16(W->w13) || !aligned16(W->w2)) return MOE_ERR_INVALID_ARG;
+  switch (W->format) {
+    case MOE_W_F32:
+      if (W->hidden % 4 || W->inter % 4) return MOE_ERR_UNSUPPORTED;
+      break;
+    case MOE_W_MXFP8:
+    case MOE_W_MXFP4:
+      if (!W->w13_scale || !W->w2_scale) return MOE_ERR_INVALID_ARG;
+      if (W->hidden % 32 || W->inter % 32) return MOE_ERR_UNSUPPORTED;
+      break;
+    case MOE_W_FP8_BLK128:
+      if (!W->w13_scale || !W->w2_scale) return MOE_ERR_INVALID_ARG;
+      if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
+      break;
+    default:
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+moe_status check_routing(const moe_weights* W, int32_t T, int32_t k) {
+  if (T < 0 || k < 0) return MOE_ERR_INVALID_ARG;
+  if (k + W->num_shared < 1) return MOE_ERR_INVALID_ARG;
+  if (k > W->num_experts) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * (k + W->num_shared) > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool grouped_supported(const moe_weights* W) {
+  return W->format == MOE_W_MXFP8 || W->format == MOE_W_MXFP4 ||
+         W->format == MOE_W_FP8_BLK128;
+}
+
+bool block_ok(int32_t bs) { return bs == 32 || bs == 64 || bs == 128; }
+
+// Grouped-path crossover: T * slots above which expert-centric packing wins.
+// Measured on gfx950 (MXFP4 4096 x 1536 x 128 experts sweep, uniform and Zipf
+// routing); other shapes use the same per-entry threshold.
+int32_t decode_entry_threshold(const moe_weights* W) {
+  (void)W;
+  return 64 * 8;
+}
+
+struct GroupedLayout {
+  size_t sorted, expert_ids, offsets, npp, as_ws, xq, xs, hq, hs, slot_out, total;
+  int32_t cap;
+};
+
+GroupedLayout grouped_layout(const moe_weights* W, int32_t T, int32_t k, int32_t bs) {
+  GroupedLayout L{};
+  const int32_t slots = k + W->num_shared;
+  const int32_t n = T * slots;
+  const int32_t n_exp = W->num_experts + W->num_shared;
+  L.cap = n + n_exp * (bs - 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  L.sorted = take((size_t)L.cap * 4);
+  L.expert_ids = take((size_t)(L.cap / bs + 1) * 4);
+  L.offsets = take((size_t)(n_exp + 1) * 4);
+  L.npp = take(4);
+  L.as_ws = take(moe::align_sort_workspace_bytes(n, n_exp));
+  L.xq = take((size_t)L.cap * W->hidden);
+  L.xs = take((size_t)L.cap * (W->hidden / 32));
+  L.hq = take((size_t)L.cap * W->inter);
+  L.hs = take((size_t)L.cap * (W->inter / 32));
+  L.slot_out = take((size_t)n * W->hidden * 4);
+  L.total = off;
+  return L;
+}
+
+size_t decode_workspace(const moe_weights* W, int32_t T, int32_t k) {
+  return align_up((size_t)T * (k + W->num_shared) * W->inter * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int32_t moe_abi_version(void) { return kAbiVersion; }
+
+int32_t moe_decode_max_entries(void) { return kDecodeMaxEntries; }
+
+moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
+                       const int32_t* topk_ids, int32_t T, int32_t k, void* h, int32_t h_dtype,
+                       void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
+  if (!dtype_ok(x_dtype) || !dtype_ok(h_dtype)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !h || (k > 0 && !topk_ids) || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * (k + W->num_shared) > kDecodeMaxEntries) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_gate_up_decode(*W, x, x_dtype, topk_ids, T, k, h, h_dtype,
+                                             as_stream(stream)));
+}
+
+moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
+                    const int32_t* topk_ids, const float* topk_weights, int32_t T, int32_t k,
+                    void* y, int32_t y_dtype, void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
+  if (!dtype_ok(h_dtype) || !dtype_ok(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!h || !y || (k > 0 && (!topk_ids || !topk_weights)) || !aligned16(h))
+    return MOE_ERR_INVALID_ARG;
+  if (h_dtype == MOE_DT_BF16 && W->format == MOE_W_F32) return MOE_ERR_UNSUPPORTED;
+  if (k + W->num_shared > 64) return MOE_ERR_UNSUPPORTED;   // one slot per lane
+  if ((int64_t)T * (k + W->num_shared) > (1 << 30)) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_down_decode(*W, h, h_dtype, topk_ids, topk_weights, T, k, y,
+                                          y_dtype, as_stream(stream)));
+}
+
+size_t moe_align_sort_capacity(int32_t T, int32_t k, int32_t num_experts, int32_t num_shared,
+                               int32_t block_size) {
+  if (T < 0 || k < 0 || num_experts < 1 || num_shared < 0 || block_size < 1) return 0;
+  return (size_t)T * (k + num_shared) + (size_t)(num_experts + num_shared) * (block_size - 1);
+}
+
+size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t num_experts,
+                                      int32_t num_shared, int32_t block_size) {
+  (void)block_size;
+  if (T < 0 || k < 0 || num_experts < 1 || num_shared < 0) return 0;
+  return moe::align_sort_workspace_bytes(T * (k + num_shared), num_experts + num_shared);
+}
+
+moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t num_experts,
+                          int32_t num_shared, int32_t block_size, int32_t* sorted_token_ids,
+                          int32_t* expert_ids, int32_t* expert_offsets,
+                          int32_t* num_tokens_post_padded, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (T < 0 || k < 0 || num_experts < 1 || (num_shared != 0 && num_shared != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (k + num_shared < 1 || k > num_experts) return MOE_ERR_INVALID_ARG;
+  if (num_experts + num_shared > kMaxExpertsTotal) return MOE_ERR_UNSUPPORTED;
+  if (block_size < 1 || block_size > 1024) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * (k + num_shared) + (int64_t)(num_experts + num_shared) * block_size >
+      INT32_MAX / 2)
+    return MOE_ERR_UNSUPPORTED;
+  if ((k > 0 && T > 0 && !topk_ids) || !sorted_token_ids || !expert_ids || !expert_offsets ||
+      !num_tokens_post_padded || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes <
+      moe_align_sort_workspace_bytes(T, k, num_experts, num_shared, block_size))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(moe::launch_align_sort(topk_ids, T, k, num_experts, num_shared, block_size,
+                                         sorted_token_ids, expert_ids, expert_offsets,
+                                         num_tokens_post_padded, workspace,
+                                         as_stream(stream)));
+}
+
+moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H, int32_t slots,
+                            const int32_t* sorted_token_ids,
+                            const int32_t* num_tokens_post_padded, int32_t capacity, uint8_t* xq,
+                            uint8_t* xs, void* stream) {
+  if (!dtype_ok(x_dtype) || T < 0 || H <= 0 || slots < 1 || capacity < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 32) return MOE_ERR_UNSUPPORTED;
+  if (capacity == 0) return MOE_OK;
+  if ((T > 0 && !x) || !sorted_token_ids || !num_tokens_post_padded || !xq || !xs)
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_gather_quant(x, x_dtype, T, H, slots, sorted_token_ids,
+                                           num_tokens_post_padded, capacity, xq, xs,
+                                           as_stream(stream)));
+}
+
+moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const uint8_t* xs,
+                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                               int32_t capacity, int32_t block_size, uint8_t* hq, uint8_t* hs,
+                               void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity == 0) return MOE_OK;
+  if (!xq || !xs || !expert_ids || !num_tokens_post_padded || !hq || !hs)
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_grouped_gate_up(*W, xq, xs, expert_ids, num_tokens_post_padded,
+                                              capacity, block_size, hq, hs, as_stream(stream)));
+}
+
+moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8_t* hs,
+                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                            const int32_t* num_tokens_post_padded, int32_t capacity,
+                            int32_t block_size, const float* topk_weights, int32_t T, int32_t k,
+                            float* slot_out, void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
+  if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (capacity == 0 || T == 0) return MOE_OK;
+  if (!hq || !hs || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !slot_out ||
+      (k > 0 && !topk_weights))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_grouped_down(*W, hq, hs, sorted_token_ids, expert_ids,
+                                           num_tokens_post_padded, capacity, block_size,
+                                           topk_weights, T, k, slot_out, as_stream(stream)));
+}
+
+moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t H, void* y,
+                       int32_t y_dtype, void* stream) {
+  if (T < 0 || slots < 1 || H <= 0 || !dtype_ok(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!slot_out || !y) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_combine(slot_out, T, slots, H, y, y_dtype, as_stream(stream)));
+}
+
+int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
+  if (check_weights(W) != MOE_OK || T < 0 || k < 0) return MOE_PATH_DECODE;
+  const int64_t entries = (int64_t)T * (k + W->num_shared);
+  if (!grouped_supported(W)) return MOE_PATH_DECODE;
+  if (W->hidden % 128 || W->inter % 64) return MOE_PATH_DECODE;
+  if (entries > kDecodeMaxEntries) return MOE_PATH_GROUPED;
+  return entries <= decode_entry_threshold(W) ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+}
+
+size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k, int32_t path,
+                                 int32_t block_size) {
+  if (check_weights(W) != MOE_OK || T < 0 || k < 0) return 0;
+  if (path == MOE_PATH_AUTO) path = moe_choose_path(W, T, k);
+  if (path == MOE_PATH_DECODE) return decode_workspace(W, T, k);
+  if (path == MOE_PATH_GROUPED && block_ok(block_size))
+    return grouped_layout(W, T, k, block_size).total;
+  return 0;
+}
+
+moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
+                     const int32_t* topk_ids, const float* topk_weights, int32_t T, int32_t k,
+                     void* y, int32_t y_dtype, int32_t path, int32_t block_size, void* workspace,
+                     size_t workspace_bytes, int32_t* chosen, void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_GROUPED)
+    return MOE_ERR_INVALID_ARG;
+  if (path == MOE_PATH_AUTO) path = moe_choose_path(W, T, k);
+  if (chosen) *chosen = path;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || (k > 0 && (!topk_ids || !topk_weights)) || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  const int32_t slots = k + W->num_shared;
+  if (path == MOE_PATH_DECODE) {
+    if (workspace_bytes < decode_workspace(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+    st = moe_gate_up(W, x, x_dtype, topk_ids, T, k, workspace, MOE_DT_F32, stream);
+    if (st != MOE_OK) return st;
+    return moe_down(W, workspace, MOE_DT_F32, topk_ids, topk_weights, T, k, y, y_dtype, stream);
+  }
+  // grouped
+  if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  const GroupedLayout L = grouped_layout(W, T, k, block_size);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARG;
+  char* ws = reinterpret_cast<char*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(ws + L.expert_ids);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* npp = reinterpret_cast<int32_t*>(ws + L.npp);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+  uint8_t* hs = reinterpret_cast<uint8_t*>(ws + L.hs);
+  float* so = reinterpret_cast<float*>(ws + L.slot_out);
+  hipError_t e = moe::launch_align_sort(topk_ids, T, k, W->num_experts, W->num_shared, block_size,
+                                        sorted, eids, offs, npp, ws + L.as_ws, s);
+  if (e != hipSuccess) return from_hip(e);
+  e = moe::launch_gather_quant(x, x_dtype, T, W->hidden, slots, sorted, npp, L.cap, xq, xs, s);
+  if (e != hipSuccess) return from_hip(e);
+  e = moe::launch_grouped_gate_up(*W, xq, xs, eids, npp, L.cap, block_size, hq, hs, s);
+  if (e != hipSuccess) return from_hip(e);
+  e = moe::launch_grouped_down(*W, hq, hs, sorted, eids, npp, L.cap, block_size, topk_weights, T,
+                               k, so, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(moe::launch_combine(so, T, slots, W->hidden, y, y_dtype, s));
+}
+
+// ---- measurement helpers -----------------------------------------------
+
+moe_status moe_util_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes % 16 || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_copy(src, dst, bytes, as_stream(stream)));
+}
+
+moe_status moe_util_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink || bytes % 16 || !aligned16(src)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_read(src, bytes, sink, as_stream(stream)));
+}
+
+int32_t moe_util_read_sink_len(void) { return moe::kReadSinkLen; }
+
+moe_status moe_util_fill(void* dst, size_t bytes, uint32_t value, void* stream) {
+  if (!dst || bytes % 16 || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_fill(dst, bytes, value, as_stream(stream)));
+}
+
+int32_t moe_util_num_cus(void) { return moe::device_num_cus(); }
+
+}  // extern "C"

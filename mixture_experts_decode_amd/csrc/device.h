@@ -1,0 +1,202 @@
+// Device-side helpers shared by the HIP kernels of this library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum WFormat { W_F32 = 0, W_MXFP8 = 1, W_MXFP4 = 2, W_FP8B128 = 3 };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// loads
+// ---------------------------------------------------------------------------
+
+// 16-byte load that bypasses reuse-oriented cache allocation: for data each
+// call reads exactly once (expert weight rows in the expert-major kernels).
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+// E8M0 scale byte -> float 2^(b-127); b = 0 is the subnormal 2^-127, b = 255 NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  uint32_t bits = b ? (b << 23) : 0x00400000u;
+  bits = (b == 255u) ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two E4M3 bytes (low or high half-word of v) -> two exact bf16 values.
+template <bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI);
+}
+
+// Two E2M1 nibbles (byte `sel` of v) -> two exact bf16 values.
+template <int SEL>
+__device__ __forceinline__ bf16x2 fp4x2_to_bf16x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, SEL);
+}
+
+// Two E4M3 bytes -> two exact floats.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, HI);
+}
+
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_to_f32x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte weight chunk . activation chunk, FP32 accumulation
+// ---------------------------------------------------------------------------
+// Elements per 16-byte weight chunk: 16 (E4M3), 32 (E2M1), 4 (F32).
+template <int FMT> struct Chunk;
+template <> struct Chunk<W_MXFP8> { static constexpr int kElems = 16; };
+template <> struct Chunk<W_FP8B128> { static constexpr int kElems = 16; };
+template <> struct Chunk<W_MXFP4> { static constexpr int kElems = 32; };
+template <> struct Chunk<W_F32> { static constexpr int kElems = 4; };
+
+// Weight chunk w against bf16 activations xs (kElems/2 dwords, element 2i in
+// the low half of dword i).  Returns the unscaled partial dot product.
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_bf16(const u32x4 w, const uint32_t* xs) {
+  float acc = 0.f;
+  if constexpr (FMT == W_MXFP8 || FMT == W_FP8B128) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc = dot2_bf16(fp8x2_to_bf16x2<false>(w[d]), as_bf16x2(xs[2 * d]), acc);
+      acc = dot2_bf16(fp8x2_to_bf16x2<true>(w[d]), as_bf16x2(xs[2 * d + 1]), acc);
+    }
+  } else if constexpr (FMT == W_MXFP4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc = dot2_bf16(fp4x2_to_bf16x2<0>(w[d]), as_bf16x2(xs[4 * d + 0]), acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<1>(w[d]), as_bf16x2(xs[4 * d + 1]), acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<2>(w[d]), as_bf16x2(xs[4 * d + 2]), acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<3>(w[d]), as_bf16x2(xs[4 * d + 3]), acc);
+    }
+  } else {  // F32 weights, bf16 activations
+    acc = fmaf(__uint_as_float(w[0]), bf16_lo(xs[0]), acc);
+    acc = fmaf(__uint_as_float(w[1]), bf16_hi(xs[0]), acc);
+    acc = fmaf(__uint_as_float(w[2]), bf16_lo(xs[1]), acc);
+    acc = fmaf(__uint_as_float(w[3]), bf16_hi(xs[1]), acc);
+  }
+  return acc;
+}
+
+// Weight chunk w against float activations xs (kElems floats).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot_f32(const u32x4 w, const float* xs) {
+  float acc = 0.f;
+  if constexpr (FMT == W_MXFP8 || FMT == W_FP8B128) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f32x2 a = fp8x2_to_f32x2<false>(w[d]);
+      f32x2 b = fp8x2_to_f32x2<true>(w[d]);
+      acc = fmaf(a.x, xs[4 * d + 0], acc);
+      acc = fmaf(a.y, xs[4 * d + 1], acc);
+      acc = fmaf(b.x, xs[4 * d + 2], acc);
+      acc = fmaf(b.y, xs[4 * d + 3], acc);
+    }
+  } else if constexpr (FMT == W_MXFP4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f32x2 a = fp4x2_to_f32x2<0>(w[d]);
+      f32x2 b = fp4x2_to_f32x2<1>(w[d]);
+      f32x2 c = fp4x2_to_f32x2<2>(w[d]);
+      f32x2 e = fp4x2_to_f32x2<3>(w[d]);
+      acc = fmaf(a.x, xs[8 * d + 0], acc);
+      acc = fmaf(a.y, xs[8 * d + 1], acc);
+      acc = fmaf(b.x, xs[8 * d + 2], acc);
+      acc = fmaf(b.y, xs[8 * d + 3], acc);
+      acc = fmaf(c.x, xs[8 * d + 4], acc);
+      acc = fmaf(c.y, xs[8 * d + 5], acc);
+      acc = fmaf(e.x, xs[8 * d + 6], acc);
+      acc = fmaf(e.y, xs[8 * d + 7], acc);
+    }
+  } else {
+    acc = fmaf(__uint_as_float(w[0]), xs[0], acc);
+    acc = fmaf(__uint_as_float(w[1]), xs[1], acc);
+    acc = fmaf(__uint_as_float(w[2]), xs[2], acc);
+    acc = fmaf(__uint_as_float(w[3]), xs[3], acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 sum: rotations inside each 16-lane row (DPP), then the gfx950 row
+// swaps across rows (permlane16/32 swap).  Fixed order; every lane ends with
+// the same total.  No LDS, no barrier.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<0x128>(x);  // row_ror:8
+  x += dpp_f32<0x124>(x);  // row_ror:4
+  x += dpp_f32<0x122>(x);  // row_ror:2
+  x += dpp_f32<0x121>(x);  // row_ror:1
+  uint32_t u = __float_as_uint(x);
+  auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  u = __float_as_uint(x);
+  auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// SiLU(g) * u in FP32.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware block order.  Workgroups are dispatched round-robin over the
+// XCDs (block b runs on XCD b % nxcd).  The returned logical index makes
+// consecutive logical blocks share an XCD (and therefore its L2), so blocks
+// that reuse the same rows sit on one L2 (align-and-sort article, Triton
+// section: pid remapping on XCDs).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks, int nxcd) {
+  int per = nblocks / nxcd;            // full rounds
+  int full = per * nxcd;
+  if (b >= full) return b;             // ragged tail keeps its order
+  return (b % nxcd) * per + b / nxcd;
+}
+
+}  // namespace moe

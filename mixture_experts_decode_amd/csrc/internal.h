@@ -1,0 +1,53 @@
+// Internal host interface between the C ABI layer (api.hip) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+namespace moe {
+
+constexpr int kDecodeMaxEntries = 2048;   // T * slots staged in LDS by gate_up
+constexpr int kMaxExpertsTotal = 1024;    // E + S
+
+int device_num_cus();
+int device_num_xcds();
+
+// decode.hip
+hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
+                                 const int32_t* ids, int T, int k, void* h, int h_dtype,
+                                 hipStream_t s);
+hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
+                              const int32_t* ids, const float* wts, int T, int k, void* y,
+                              int y_dtype, hipStream_t s);
+
+// align_sort.hip
+size_t align_sort_workspace_bytes(int n_entries, int n_experts);
+hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int bs,
+                             int32_t* sorted, int32_t* expert_ids, int32_t* offsets,
+                             int32_t* npp, void* ws, hipStream_t s);
+
+// grouped.hip
+hipError_t launch_gather_quant(const void* x, int x_dtype, int T, int H, int slots,
+                               const int32_t* sorted, const int32_t* npp, int capacity,
+                               uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const uint8_t* xs,
+                                  const int32_t* expert_ids, const int32_t* npp, int capacity,
+                                  int bs, uint8_t* hq, uint8_t* hs, hipStream_t s);
+hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const uint8_t* hs,
+                               const int32_t* sorted, const int32_t* expert_ids,
+                               const int32_t* npp, int capacity, int bs, const float* wts,
+                               int T, int k, float* slot_out, hipStream_t s);
+hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* y, int y_dtype,
+                          hipStream_t s);
+
+// util.hip
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_fill(void* dst, size_t bytes, uint32_t value, hipStream_t s);
+constexpr int kReadSinkLen = 4096;
+
+}  // namespace moe

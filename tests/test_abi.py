@@ -1,0 +1,124 @@
+"""The C-ABI library loads and exports every function the public headers
+declare; host-side argument checks return their status codes before any
+launch.  No compute call is made here (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe_mi355x.h", "moe_mi355x_util.h")]
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mixture_experts_decode_amd as moe
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_mi355x.so is not built (run python -m mixture_experts_decode_amd.build)")
+    return moe.load()
+
+
+def test_headers_declare_the_boundary():
+    names = declared_functions()
+    for need in ("moe_align_sort", "moe_gate_up", "moe_down", "moe_layer", "moe_status_string",
+                 "moe_gather_quant", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
+                 "moe_choose_path", "moe_layer_workspace_bytes", "moe_util_copy"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import mixture_experts_decode_amd as moe
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding knows every one of them too
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_status_strings_and_sizes(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.moe_abi_version() == 1
+    # capacity = T*(k+S) + (E+S)*(BS-1)
+    assert lib.moe_align_sort_capacity(16384, 8, 256, 0, 128) == 131072 + 256 * 127
+    assert lib.moe_align_sort_capacity(3, 2, 4, 0, 4) == 6 + 4 * 3
+    assert lib.moe_align_sort_capacity(4, 8, 256, 1, 64) == 36 + 257 * 63
+
+
+def _weights(moe, **kw):
+    d = dict(hidden=2048, inter=768, num_experts=128, num_shared=0, format=1,
+             w13=16, w13_scale=16, w2=16, w2_scale=16)
+    d.update(kw)
+    return moe._Weights(**d)
+
+
+def test_host_argument_errors(lib):
+    import mixture_experts_decode_amd as moe
+    P = ctypes.c_void_p
+    dummy = P(4096)
+    # null weights
+    assert lib.moe_gate_up(None, dummy, 1, dummy, 4, 8, dummy, 0, None) == moe.ERR_INVALID_ARG
+    w = _weights(moe)
+    # bad dtype enum, negative T, k > E
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 7, dummy, 4, 8, dummy, 0, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, -1, 8, dummy, 0, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 4, 200, dummy, 0, None) == moe.ERR_INVALID_ARG
+    # too many entries for the decode kernels
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 4096, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
+    # f32 activations with quantised weights
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 0, dummy, 4, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
+    # misaligned weight pointer, bad format, non-multiple-of-32 hidden
+    assert lib.moe_down(ctypes.byref(_weights(moe, w13=17)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
+                        None) == moe.ERR_INVALID_ARG
+    assert lib.moe_down(ctypes.byref(_weights(moe, format=9)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
+                        None) == moe.ERR_INVALID_ARG
+    assert lib.moe_down(ctypes.byref(_weights(moe, hidden=2050)), dummy, 0, dummy, dummy, 4, 8, dummy,
+                        0, None) == moe.ERR_UNSUPPORTED
+    # missing scales for a quantised format
+    assert lib.moe_down(ctypes.byref(_weights(moe, w2_scale=None)), dummy, 0, dummy, dummy, 4, 8, dummy,
+                        0, None) == moe.ERR_INVALID_ARG
+    # T == 0 is a no-op
+    assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 0, 8, dummy, 0, None) == moe.OK
+    # align-sort: block size, workspace
+    assert lib.moe_align_sort(dummy, 4, 8, 128, 0, 0, dummy, dummy, dummy, dummy, dummy, 1 << 20,
+                              None) == moe.ERR_INVALID_ARG
+    assert lib.moe_align_sort(dummy, 4, 8, 128, 0, 64, dummy, dummy, dummy, dummy, dummy, 4,
+                              None) == moe.ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_align_sort(dummy, 4, 8, 2000, 0, 64, dummy, dummy, dummy, dummy, dummy, 1 << 20,
+                              None) == moe.ERR_UNSUPPORTED
+    # layer: workspace too small, bad path, grouped with a bad block size
+    assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 1, 64, dummy, 16,
+                         None, None) == moe.ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 5, 64, dummy, 16,
+                         None, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 2, 48, dummy,
+                         1 << 30, None, None) == moe.ERR_UNSUPPORTED
+    # grouped steps reject fp32 weights
+    assert lib.moe_grouped_gate_up(ctypes.byref(_weights(moe, format=0)), dummy, dummy, dummy, dummy,
+                                   64, 64, dummy, dummy, None) == moe.ERR_UNSUPPORTED
+
+
+def test_path_choice_host_logic(lib):
+    w = _weights(__import__("mixture_experts_decode_amd"))
+    DEC, GRP = 1, 2
+    assert lib.moe_choose_path(ctypes.byref(w), 1, 8) == DEC
+    assert lib.moe_choose_path(ctypes.byref(w), 32, 8) == DEC
+    assert lib.moe_choose_path(ctypes.byref(w), 16384, 8) == GRP
+    # fp32 weights have no grouped path
+    w32 = _weights(__import__("mixture_experts_decode_amd"), format=0)
+    assert lib.moe_choose_path(ctypes.byref(w32), 16384, 8) == DEC
+    # workspace sizes: decode = T*slots*I*4 rounded up to 256
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * 768 * 4
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 64) > 0
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 48) == 0

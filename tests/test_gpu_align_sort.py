@@ -1,0 +1,84 @@
+"""Align-and-sort on the GPU, bit-exact against the oracle on the defined
+range: sorted_token_ids[:npp], expert_ids[:npp/BS], expert_offsets, npp."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import align_sort as A
+
+pytestmark = pytest.mark.gpu
+
+
+def _flat_ids(ids, num_experts, num_shared):
+    if not num_shared:
+        return ids.reshape(-1)
+    t = ids.shape[0]
+    return np.concatenate([ids, np.full((t, 1), num_experts, dtype=ids.dtype)], axis=1).reshape(-1)
+
+
+def _check(lib, ids, num_experts, num_shared, bs):
+    out = lib.align_sort(torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda(),
+                         num_experts, num_shared, bs)
+    torch.cuda.synchronize()
+    ref = A.align_sort(_flat_ids(ids, num_experts, num_shared), num_experts + num_shared, bs)
+    npp = int(out["num_tokens_post_padded"].item())
+    assert npp == ref["num_tokens_post_padded"]
+    assert np.array_equal(out["expert_offsets"].cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(out["sorted_token_ids"][:npp].cpu().numpy(), ref["sorted_token_ids"])
+    assert np.array_equal(out["expert_ids"][:npp // bs].cpu().numpy(), ref["expert_ids"])
+    assert npp <= out["capacity"]
+    return out
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+def test_tiny_config(lib, bs):
+    cfg = W.CONFIGS[1]
+    ids, _ = W.routing(cfg, 4)
+    _check(lib, ids, cfg.num_experts, 0, bs)
+
+
+@pytest.mark.parametrize("bs", [64, 128])
+def test_prefill_zipf_full_size(lib, bs):
+    cfg = W.CONFIGS[4]
+    ids, _ = W.routing(cfg, 16384)
+    _check(lib, ids, cfg.num_experts, 0, bs)
+
+
+@pytest.mark.parametrize("t,bs", [(1, 32), (7, 16), (256, 64), (1000, 128)])
+def test_shared_expert_entries(lib, t, bs):
+    cfg = W.CONFIGS[3]
+    ids, _ = W.routing(cfg, t)
+    _check(lib, ids, cfg.num_experts, 1, bs)
+
+
+@pytest.mark.parametrize("t", [1, 3, 64, 333, 4096])
+def test_uniform_ragged(lib, t):
+    cfg = W.CONFIGS[2]
+    ids, _ = W.routing(cfg, t)
+    _check(lib, ids, cfg.num_experts, 0, 32)
+
+
+def test_edge_cases(lib):
+    # every entry on one expert, block size 1, a single block, empty batch
+    ids = np.full((50, 2), 3, dtype=np.int32)
+    _check(lib, ids, 8, 0, 1)
+    _check(lib, ids, 8, 0, 128)
+    out = _check(lib, np.zeros((0, 8), dtype=np.int32), 16, 0, 64)
+    assert int(out["num_tokens_post_padded"].item()) == 0
+    # the largest expert count the kernels stage on chip
+    rng = np.random.default_rng(0)
+    ids = rng.integers(0, 1024, size=(300, 3)).astype(np.int32)
+    _check(lib, ids, 1024, 0, 16)
+
+
+def test_repeatable(lib):
+    cfg = W.CONFIGS[4]
+    ids, _ = W.routing(cfg, 4096)
+    d = torch.from_numpy(ids).cuda()
+    a = lib.align_sort(d, cfg.num_experts, 0, 64)
+    b = lib.align_sort(d, cfg.num_experts, 0, 64)
+    torch.cuda.synchronize()
+    n = int(a["num_tokens_post_padded"].item())
+    assert torch.equal(a["sorted_token_ids"][:n], b["sorted_token_ids"][:n])

@@ -1,0 +1,162 @@
+"""Decode-path parity on the GPU: moe_gate_up / moe_down / moe_layer(DECODE)
+against the float64 oracle (mode "none"), element by element for h and per
+token for y (cosine >= 0.99999, relative L2 <= 5e-3), plus batch invariance,
+run-to-run determinism and full-write checks."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import layer as L
+from _helpers import (assert_layer_close, device_routing, device_weights, inputs, oracle_kw,
+                      to_device_x, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+# reduced-expert variants: full H and I (so rows span every lane and several
+# chunks), fewer experts so the oracle stays fast; odd token counts give a
+# ragged tail of (token, slot) entries
+SMALL = {
+    "f32": W.CONFIGS[1],
+    "mxfp8": W.CONFIGS[2].replace(num_experts=16, tag=21),
+    "mxfp4": W.CONFIGS[5].replace(num_experts=16, tag=22),
+    "fp8_blk128": W.CONFIGS[3].replace(num_experts=12, tag=23),
+}
+
+
+def _run_decode(moe, cfg, t, h_dtype="f32", y_dtype="f32", kind=None, variant=0):
+    x, ids, w = inputs(cfg, t, kind=kind, variant=variant)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    h = moe.gate_up(Wd, xd, idd, h_dtype=h_dtype)
+    y = moe.down(Wd, h, idd, wd, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    return x, ids, w, h, y
+
+
+def _oracle(cfg, x, ids, w):
+    x64 = L.activations_f64(x, cfg.act)
+    kw = oracle_kw(cfg)
+    return L.gate_up(x64, ids, **kw), L.moe_layer(x64, ids, w, **kw)
+
+
+@pytest.mark.parametrize("fmt", list(SMALL))
+@pytest.mark.parametrize("t", [1, 5, 32])
+def test_decode_parity_small(lib, fmt, t):
+    cfg = SMALL[fmt]
+    if fmt == "f32" and t == 32:
+        t = 4
+    x, ids, w, h, y = _run_decode(lib, cfg, t)
+    h_ref, y_ref = _oracle(cfg, x, ids, w)
+    hh = to_f64(h)
+    # each h scalar: FP32 accumulation of exact products over H terms
+    scale = np.sqrt(np.mean(h_ref ** 2))
+    assert np.max(np.abs(hh - h_ref)) <= 2e-4 * scale + 1e-6, np.max(np.abs(hh - h_ref)) / scale
+    assert_layer_close(to_f64(y), y_ref, (fmt, t))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8_blk128"])
+def test_decode_bf16_intermediate_and_output(lib, fmt):
+    cfg = SMALL[fmt]
+    x, ids, w, h, y = _run_decode(lib, cfg, 7, h_dtype="bf16", y_dtype="bf16")
+    assert h.dtype == torch.bfloat16 and y.dtype == torch.bfloat16
+    _, y_ref = _oracle(cfg, x, ids, w)
+    assert_layer_close(to_f64(y), y_ref, fmt)
+
+
+def test_down_alone_on_given_h(lib):
+    """moe_down on a generated h (not one from moe_gate_up) against the
+    oracle's down product of the same h."""
+    cfg = SMALL["mxfp8"]
+    t = 9
+    _, ids, w = inputs(cfg, t)
+    h = W.hidden_states(cfg, t)
+    Wd = device_weights(cfg)
+    idd, wd = device_routing(ids, w)
+    y = lib.down(Wd, torch.from_numpy(h).cuda(), idd, wd)
+    ref = L.down(h.astype(np.float64), ids, w, **oracle_kw(cfg))
+    assert_layer_close(to_f64(y), ref)
+
+
+def test_batch_invariance_and_determinism(lib):
+    """Each output is produced by one wavefront in a fixed order, so a token's
+    h and y do not depend on the rest of the batch and repeat bit for bit."""
+    cfg = SMALL["mxfp8"]
+    x, ids, w = inputs(cfg, 32)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    h_all = lib.gate_up(Wd, xd, idd)
+    y_all = lib.down(Wd, h_all, idd, wd)
+    h_again = lib.gate_up(Wd, xd, idd)
+    y_again = lib.down(Wd, h_again, idd, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(h_all, h_again) and torch.equal(y_all, y_again)
+    for t in (0, 13, 31):
+        h1 = lib.gate_up(Wd, xd[t:t + 1].contiguous(), idd[t:t + 1].contiguous())
+        y1 = lib.down(Wd, h1, idd[t:t + 1].contiguous(), wd[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(h1[0], h_all[t]) and torch.equal(y1[0], y_all[t]), t
+
+
+def test_every_output_written(lib):
+    cfg = SMALL["mxfp4"]
+    x, ids, w = inputs(cfg, 11)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    h = torch.full((11, cfg.top_k, cfg.inter), float("nan"), device="cuda")
+    y = torch.full((11, cfg.hidden), float("nan"), device="cuda")
+    lib.gate_up(Wd, xd, idd, h=h)
+    lib.down(Wd, h, idd, wd, y=y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all() and torch.isfinite(y).all()
+
+
+def test_layer_decode_path_matches_oracle(lib):
+    cfg = SMALL["fp8_blk128"].replace(num_shared=1)
+    x, ids, w = inputs(cfg, 6)
+    Wd = device_weights(cfg)
+    y, chosen = lib.layer(Wd, to_device_x(cfg, x), *device_routing(ids, w), path="decode")
+    torch.cuda.synchronize()
+    assert chosen == "decode"
+    _, y_ref = _oracle(cfg, x, ids, w)
+    assert_layer_close(to_f64(y), y_ref)
+
+
+def test_duplicate_ids_within_a_token(lib):
+    """Two slots of one token on the same expert are legal and both count."""
+    cfg = SMALL["mxfp8"]
+    x, ids, w = inputs(cfg, 4)
+    ids = ids.copy()
+    ids[:, 1] = ids[:, 0]
+    Wd = device_weights(cfg)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd)
+    y = lib.down(Wd, h, idd, wd)
+    torch.cuda.synchronize()
+    _, y_ref = _oracle(cfg, x, ids, w)
+    assert_layer_close(to_f64(y), y_ref)
+
+
+# ---- full-size workloads, sampled tokens ---------------------------------
+
+FULL = [(2, 32, None), (2, 1, None), (3, 16, None), (5, 64, None), (5, 32, "zipf")]
+
+
+@pytest.mark.parametrize("cid,t,kind", FULL)
+def test_decode_full_size_sampled(lib, cid, t, kind):
+    """Full configuration and batch, in the launch shape the benchmark times;
+    the oracle checks a sample of tokens (tokens are independent)."""
+    cfg = W.CONFIGS[cid]
+    if kind == "zipf":
+        cfg = cfg.replace(zipf_s=1.2)
+    x, ids, w, h, y = _run_decode(lib, cfg, t, kind=kind)
+    sample = sorted({0, t // 2, t - 1})
+    x64 = L.activations_f64(x[sample], cfg.act)
+    ref = L.moe_layer(x64, ids[sample], w[sample], **oracle_kw(cfg))
+    assert_layer_close(to_f64(y)[sample], ref, (cid, t))
