@@ -111,7 +111,7 @@ def main():
         u = len(W.touched_experts(cfg, ids))
         io = b * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes + b * cfg.hidden * 4
         gate_up_bytes = u * (ebytes - ebytes_down(cfg)) + b * cfg.hidden * act_bytes + ids.nbytes \
-            + b * (cfg.top_k + cfg.num_shared) * cfg.inter * 4
+            + b * (cfg.top_k + cfg.num_shared) * cfg.inter * (4 if cfg.fmt == "f32" else 2)
         return dict(x=xd, ids=torch.from_numpy(ids).to(dev), wts=torch.from_numpy(wts).to(dev),
                     bytes=u * ebytes + io, gate_up_bytes=gate_up_bytes, U=u)
 
@@ -147,14 +147,19 @@ def main():
         read_peak = n / (best_r * 1e-3) / 1e12
         del src, dst
 
+    h_dtype = "f32" if cfg.fmt == "f32" else "bf16"   # as moe_layer's decode path
+
     def run_steps(b, steps, warmup, path):
         ins = [make_inputs(b, v) for v in range(n_layers)]
         need = moe.layer_workspace_bytes(layers[0], b, cfg.top_k, path, args.block)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         y = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
         chosen = moe.choose_path(layers[0], b, cfg.top_k) if path == "auto" else path
-        h = torch.empty((b, cfg.top_k + cfg.num_shared, cfg.inter), dtype=torch.float32,
-                        device=dev)
+        h = torch.empty((b, cfg.top_k + cfg.num_shared, cfg.inter),
+                        dtype=torch.float32 if h_dtype == "f32" else torch.bfloat16, device=dev)
+        variant = "expert" if b >= 4 else "token"
+        dws = torch.empty(max(16, (cfg.top_k + cfg.num_shared) * b * cfg.hidden * 4),
+                          dtype=torch.uint8, device=dev)
 
         def step(i, ev=None):
             L = layers[i % n_layers]
@@ -165,12 +170,20 @@ def main():
                 moe.gate_up(L, d["x"], d["ids"], h=h)
                 if ev is not None:
                     ev[1].record(stream)
-                moe.down(L, h, d["ids"], d["wts"], y=y)
+                moe.down(L, h, d["ids"], d["wts"], y=y, variant=variant, workspace=dws)
                 if ev is not None:
                     ev[2].record(stream)
             else:
                 moe.layer(L, d["x"], d["ids"], d["wts"], path="grouped", block=args.block, y=y,
                           workspace=ws)
+
+        if chosen == "decode":
+            # the timed kernel sequence is exactly moe_layer's decode path
+            step(0)
+            y_ref, _ = moe.layer(layers[0], ins[0]["x"], ins[0]["ids"], ins[0]["wts"], path="decode")
+            torch.cuda.synchronize()
+            if not torch.equal(y, y_ref):
+                raise RuntimeError("timed decode sequence differs from moe_layer(decode)")
 
         for i in range(warmup):
             step(i)

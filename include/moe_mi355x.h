@@ -131,17 +131,30 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
  * moe_down: y[t][d] = sum_j w_tj * (Wd[e_tj][d,:] . h[t][j][:]) for every
  * token t < T and output d < H (warp-decode post, section on how the two
  * kernels work: one wavefront per output dimension of a token walks all of
- * the token's experts, folds each routing weight into one FP32 accumulator and
- * finishes with a butterfly reduction; the combine is part of the projection).
- * The slots are summed into per-lane accumulators in slot order; y has no
- * intermediate buffer.
+ * the token's experts, folds each routing weight in and finishes with a
+ * butterfly reduction; the combine is part of the projection).
+ * Each slot's dot product is computed by a fixed group of lanes in a fixed
+ * order, multiplied by w_tj, and the slots are added in slot order.  Two
+ * launch shapes give identical bits:
+ *   workspace == NULL  token-major: a wavefront owns (token, output rows) and
+ *                      sums the slots in registers; nothing is buffered;
+ *   workspace != NULL  expert-major: a wavefront owns (expert, output rows),
+ *                      reads those rows once for all tokens routed to the
+ *                      expert and stores w * dot per (token, slot) in the
+ *                      workspace; a combine kernel adds them in slot order.
  *   h            device, [T][slots][I], h_dtype
  *   topk_ids     device, [T][k] int32; topk_weights device, [T][k] float32
  *   y            device, [T][H], y_dtype
+ *   workspace    device or NULL; if not NULL at least
+ *                moe_down_workspace_bytes(W, T, k) bytes, 16-byte aligned
+ * slots must be <= 64.
  */
+size_t moe_down_workspace_bytes(const moe_weights* W, int32_t T, int32_t k);
+
 moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
                     const int32_t* topk_ids, const float* topk_weights,
-                    int32_t T, int32_t k, void* y, int32_t y_dtype, void* stream);
+                    int32_t T, int32_t k, void* y, int32_t y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* Align-and-sort (expert-centric front end).                          */

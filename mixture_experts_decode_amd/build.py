@@ -20,9 +20,12 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed FP32 instructions are switched off for all device code.
+# Packed FP32 instructions are switched off for all device code.  Floating
+# point contraction is off: every fused multiply-add in the kernels is an
+# explicit fmaf or dot instruction, so equal formulas give equal bits in every
+# kernel that evaluates them.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
 
 

@@ -104,8 +104,19 @@ GroupedLayout grouped_layout(const moe_weights* W, int32_t T, int32_t k, int32_t
   return L;
 }
 
+// The decode path keeps h in BF16 (FP32 with FP32 weights), the precision of
+// the warp-decode post's activations (accuracy section).
+int32_t decode_h_dtype(const moe_weights* W) {
+  return W->format == MOE_W_F32 ? MOE_DT_F32 : MOE_DT_BF16;
+}
+
+size_t decode_h_bytes(const moe_weights* W, int32_t T, int32_t k) {
+  const size_t el = decode_h_dtype(W) == MOE_DT_BF16 ? 2 : 4;
+  return align_up((size_t)T * (k + W->num_shared) * W->inter * el);
+}
+
 size_t decode_workspace(const moe_weights* W, int32_t T, int32_t k) {
-  return align_up((size_t)T * (k + W->num_shared) * W->inter * 4);
+  return decode_h_bytes(W, T, k) + align_up((size_t)T * (k + W->num_shared) * W->hidden * 4);
 }
 
 }  // namespace
@@ -142,9 +153,15 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
                                              as_stream(stream)));
 }
 
+size_t moe_down_workspace_bytes(const moe_weights* W, int32_t T, int32_t k) {
+  if (check_weights(W) != MOE_OK || T < 0 || k < 0) return 0;
+  return (size_t)T * (k + W->num_shared) * W->hidden * sizeof(float);
+}
+
 moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
                     const int32_t* topk_ids, const float* topk_weights, int32_t T, int32_t k,
-                    void* y, int32_t y_dtype, void* stream) {
+                    void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   moe_status st = check_weights(W);
   if (st != MOE_OK) return st;
   if ((st = check_routing(W, T, k)) != MOE_OK) return st;
@@ -154,9 +171,15 @@ moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
     return MOE_ERR_INVALID_ARG;
   if (h_dtype == MOE_DT_BF16 && W->format == MOE_W_F32) return MOE_ERR_UNSUPPORTED;
   if (k + W->num_shared > 64) return MOE_ERR_UNSUPPORTED;   // one slot per lane
-  if ((int64_t)T * (k + W->num_shared) > (1 << 30)) return MOE_ERR_UNSUPPORTED;
+  if (moe::down_lanes_per_row(W->format, W->inter, h_dtype) == 0) return MOE_ERR_UNSUPPORTED;
+  if (workspace) {
+    if (workspace_bytes < moe_down_workspace_bytes(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * (k + W->num_shared) > kDecodeMaxEntries) return MOE_ERR_UNSUPPORTED;
+  }
   return from_hip(moe::launch_down_decode(*W, h, h_dtype, topk_ids, topk_weights, T, k, y,
-                                          y_dtype, as_stream(stream)));
+                                          y_dtype, reinterpret_cast<float*>(workspace),
+                                          as_stream(stream)));
 }
 
 size_t moe_align_sort_capacity(int32_t T, int32_t k, int32_t num_experts, int32_t num_shared,
@@ -295,9 +318,15 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   if (path == MOE_PATH_DECODE) {
     if (workspace_bytes < decode_workspace(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
-    st = moe_gate_up(W, x, x_dtype, topk_ids, T, k, workspace, MOE_DT_F32, stream);
+    const int32_t hdt = decode_h_dtype(W);
+    st = moe_gate_up(W, x, x_dtype, topk_ids, T, k, workspace, hdt, stream);
     if (st != MOE_OK) return st;
-    return moe_down(W, workspace, MOE_DT_F32, topk_ids, topk_weights, T, k, y, y_dtype, stream);
+    // expert-major down from a few tokens up (identical results either way)
+    char* so = reinterpret_cast<char*>(workspace) + decode_h_bytes(W, T, k);
+    const bool em = moe::down_expert_major(T);
+    return moe_down(W, workspace, hdt, topk_ids, topk_weights, T, k, y, y_dtype,
+                    em ? so : nullptr, em ? workspace_bytes - decode_h_bytes(W, T, k) : 0,
+                    stream);
   }
   // grouped
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;

@@ -3,23 +3,34 @@
 // Both follow the warp-decode post (sections on how the two kernels work and
 // on warp independence): every output scalar is owned by exactly one 64-lane
 // wavefront, which streams the expert weight rows it needs, converts the
-// stored format to FP32/BF16 in registers, keeps FP32 accumulators and finishes
-// with a wave reduction; nothing is staged between kernels except h itself.
+// stored format to BF16/FP32 in registers, keeps FP32 accumulators and
+// finishes with a fixed-order cross-lane reduction.
 //
 // gfx950-specific choices (not on the pages):
-//  * gate_up is expert-major: a wavefront owns NR neurons (gate + up rows) of
-//    one touched expert and produces them for every (token, slot) routed to
-//    that expert in the batch, so each weight row is read from HBM once per
-//    call even when several tokens share an expert.  Each workgroup finds the
-//    touched experts itself from the routed ids (an LDS bitmask), so no
-//    pre-pass kernel and no host sync are needed; waves loop over
-//    (expert rank, neuron group) items with a static stride.
-//  * down is token-major as on the page, with the (slot, K-chunk) pairs of a
-//    token flattened across the 64 lanes, and workgroups of one output group
-//    ordered onto one XCD so tokens sharing an expert hit that XCD's L2.
-//  * 16-byte loads per lane; E4M3 / E2M1 are converted to exact BF16 and
-//    multiplied with BF16 activations by v_dot2_f32_bf16 (FP32 accumulate); the
-//    MX / tile scale multiplies each 16-byte chunk's partial sum.
+//  * gate_up is expert-major: a wavefront owns NR neurons (their gate and up
+//    rows) of one touched expert and produces them for every (token, slot)
+//    routed to that expert in the batch, so each weight row is read from HBM
+//    once per call even when several tokens share an expert.  Each workgroup
+//    finds the touched experts itself from the routed ids (LDS bitmask), so
+//    no pre-pass kernel and no host sync are needed; wavefronts loop over
+//    (expert rank, neuron group) items with a static stride, prefetching the
+//    next item's rows and the next token's activation chunk.
+//  * down has two variants with bitwise-identical results.  In both, a row of
+//    W_down is split over LPR lanes (8 or 16) so one wavefront covers 64/LPR
+//    output rows and every dot product is reduced inside a DPP row.
+//      - token-major (as on the page): a wavefront owns (token, output rows)
+//        and folds the token's slots in slot order into y; no buffer at all.
+//      - expert-major: a wavefront owns (expert, output rows), reads those
+//        rows once and writes w * dot for every (token, slot) routed to the
+//        expert; a small combine kernel then sums the slots in slot order.
+//        Used from a few tokens up, because rows shared by several tokens do
+//        not survive in the 4 MB per-XCD L2 between the tokens' reads.
+//  * 16-byte loads per lane; E4M3 / E2M1 are converted exactly to BF16 and
+//    multiplied with BF16 activations by v_dot2_f32_bf16, or converted to FP32
+//    for FP32 intermediates; the MX / tile scale multiplies each 16-byte
+//    chunk's partial sum.
+
+#include <cstdlib>
 
 #include "device.h"
 #include "internal.h"
@@ -31,6 +42,13 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaskWords = kMaxExpertsTotal / 32;
+
+// Occupancy floor for the streaming kernels: at least WPE wavefronts per SIMD
+// (4 -> <= 128 VGPRs), so latency is hidden by resident waves rather than by
+// registers the compiler would otherwise spend on hoisted loads; 2 for the
+// shapes that keep long rows (or a prefetched second item) in registers.
+#define MOE_STREAM_KERNEL(WPE) \
+  __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(WPE)))
 
 struct GateUpArgs {
   const uint8_t* w13;
@@ -44,6 +62,7 @@ struct GateUpArgs {
   int n_groups;     // neuron groups per expert
   int n_words;      // 32-bit words of the touched-expert mask
   int n_entries;    // T * slots
+  uint32_t slots_magic;  // ceil(2^32 / slots): entry / slots by a multiply-high
 };
 
 struct DownArgs {
@@ -52,22 +71,90 @@ struct DownArgs {
   const void* h;
   const int32_t* ids;
   const float* wts;
-  void* y;
+  void* y;          // token-major: y [T][H]; expert-major: slot_out [T*slots][H] f32
   int T, k, slots, E, H, I;
   int row_bytes;    // bytes of one w2 row
   int chunks;       // 16-byte chunks per w2 row
-  int F;            // slots * chunks (flattened per-token chunks)
-  int n_dgroups;    // output groups of ND rows
+  int cpl;          // chunks per lane = chunks / LPR
+  int n_dgroups;    // output groups of 64/LPR rows
+  int n_words;
+  int n_entries;
   int nxcd;
+  uint32_t slots_magic;
+  int rpl;          // rows per lane group in the expert-major kernel
 };
+
+// entry / slots for entry < 2^24 (slots <= 64): exact with a 32-bit reciprocal.
+__device__ __forceinline__ int div_slots(int v, uint32_t magic) {
+  return (int)(((unsigned long long)(unsigned)v * magic) >> 32);
+}
 
 __device__ __forceinline__ int clamp_expert(int e, int n) {
   return (unsigned)e < (unsigned)n ? e : 0;
 }
 
-// Scale of 16-byte chunk c of weight row `row` (global row index over
-// [experts][projections][rows]); `blk_row` is the row's 128-tile row index for
-// FP8B128, `blk_rows_base` the tile-row base of its matrix.
+// Stage the batch's routed experts in LDS (entry index t*slots + j -> expert,
+// the shared slot being expert E) and the bitmask of touched experts.
+// Returns the number of touched experts.  Whole workgroup; two barriers.
+__device__ __forceinline__ int stage_routing(const int32_t* ids, int k, int slots, int E,
+                                             int n_words, int n_entries, int* s_ids,
+                                             uint32_t* s_mask) {
+  const int tid = threadIdx.x;
+  for (int q = tid; q < n_words; q += kBlock) s_mask[q] = 0;
+  __syncthreads();
+  for (int v = tid; v < n_entries; v += kBlock) {
+    const int t = v / slots, j = v - t * slots;
+    const int e = j < k ? clamp_expert(ids[t * k + j], E) : E;
+    s_ids[v] = e;
+    atomicOr(&s_mask[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  int u = 0;
+  for (int q = 0; q < n_words; ++q) u += __popc(s_mask[q]);
+  return u;
+}
+
+// r-th set bit over the LDS mask words (uniform inputs).
+__device__ __forceinline__ int select_rank(const uint32_t* mask, int n_words, int r) {
+  int q = 0;
+  uint32_t m = 0;
+  for (; q < n_words; ++q) {
+    m = mask[q];
+    const int c = __popc(m);
+    if (r < c) break;
+    r -= c;
+  }
+  for (int i = 0; i < r; ++i) m &= m - 1;
+  return q * 32 + __ffs(m) - 1;
+}
+
+// Walks the entries routed to one expert, in ascending entry order.
+struct PairIter {
+  int base;
+  unsigned long long bm;
+};
+
+__device__ __forceinline__ void pairs_begin(PairIter& it, const int* s_ids, int n, int e) {
+  const int lane = threadIdx.x & (kWave - 1);
+  it.base = 0;
+  it.bm = __ballot(lane < n && s_ids[lane] == e);
+}
+
+__device__ __forceinline__ int pairs_next(PairIter& it, const int* s_ids, int n, int e) {
+  const int lane = threadIdx.x & (kWave - 1);
+  while (it.bm == 0) {
+    it.base += kWave;
+    if (it.base >= n) return -1;
+    const int v = it.base + lane;
+    it.bm = __ballot(v < n && s_ids[v] == e);
+  }
+  const int b = __ffsll((long long)it.bm) - 1;
+  it.bm &= it.bm - 1;
+  return it.base + b;
+}
+
+// Scale of 16-byte chunk c of weight row `row`; `tile_row` is the row's
+// 128-tile row (FP8 with 128x128 tiles).
 template <int FMT>
 __device__ __forceinline__ float chunk_scale(const void* scales, long long row, int c,
                                              int scale_row_len, long long tile_row) {
@@ -97,7 +184,7 @@ __device__ __forceinline__ void load_x_chunk(XChunk<FMT, XF32>& xc, const void* 
   if constexpr (W >= 4) {
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
-      u32x4 q = load16(p + 4 * i);
+      const u32x4 q = load16(p + 4 * i);
       xc.v[4 * i + 0] = q[0];
       xc.v[4 * i + 1] = q[1];
       xc.v[4 * i + 2] = q[2];
@@ -119,137 +206,269 @@ __device__ __forceinline__ float chunk_dot(const u32x4 w, const XChunk<FMT, XF32
   }
 }
 
-// r-th set bit over the LDS mask words (uniform inputs).
-__device__ __forceinline__ int select_rank(const uint32_t* mask, int n_words, int r) {
-  int q = 0;
-  uint32_t m = 0;
-  for (; q < n_words; ++q) {
-    m = mask[q];
-    int c = __popc(m);
-    if (r < c) break;
-    r -= c;
+// ---------------------------------------------------------------------------
+// gate_up
+// ---------------------------------------------------------------------------
+
+// Rows of one item.  PRE: held as exact BF16 pairs (converted once per item,
+// reused by every token routed to the expert); otherwise the raw 16-byte
+// chunks, converted per token.
+template <int FMT, int NR, int MCH, bool PRE>
+struct GateRows {
+  static constexpr int kWords = PRE ? Chunk<FMT>::kElems / 2 : 4;
+  uint32_t w[2 * NR][MCH][kWords];
+  float s[2 * NR][MCH];
+};
+
+template <int FMT>
+__device__ __forceinline__ void chunk_to_bf16(const u32x4 q, uint32_t* out) {
+  if constexpr (FMT == W_MXFP4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      out[4 * d + 0] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<0>(q[d]));
+      out[4 * d + 1] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<1>(q[d]));
+      out[4 * d + 2] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<2>(q[d]));
+      out[4 * d + 3] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<3>(q[d]));
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      out[2 * d + 0] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(q[d]));
+      out[2 * d + 1] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(q[d]));
+    }
   }
-  for (int i = 0; i < r; ++i) m &= m - 1;
-  return q * 32 + __ffs(m) - 1;
 }
 
-template <int FMT, int NR, int MCH, bool XF32, bool HBF16>
-__global__ __launch_bounds__(kBlock) void gate_up_decode_kernel(const GateUpArgs a) {
+// GUARD: the row has fewer than 64*MCH chunks, lanes past the end hold zeros.
+template <int FMT, int NR, int MCH, bool PRE, bool GUARD>
+__device__ __forceinline__ void load_gate_rows(GateRows<FMT, NR, MCH, PRE>& R,
+                                               const GateUpArgs& a, int e, int n0, int lane) {
+  u32x4 raw[2 * NR][MCH];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      const int n = min(n0 + rr, a.I - 1);
+      const long long row = ((long long)e * 2 + p) * a.I + n;
+      const long long tile_row = ((long long)e * 2 + p) * (a.I >> 7) + (n >> 7);
+      const uint8_t* base = a.w13 + row * a.row_bytes;
+#pragma unroll
+      for (int m = 0; m < MCH; ++m) {
+        const int c = lane + m * kWave;
+        if (!GUARD || c < a.chunks) {
+          raw[p * NR + rr][m] = load_stream16(base + (size_t)c * 16);
+          R.s[p * NR + rr][m] = chunk_scale<FMT>(
+              a.w13s, row, c, FMT == W_FP8B128 ? (a.H >> 7) : (a.H >> 5), tile_row);
+        } else {
+          raw[p * NR + rr][m] = u32x4{0, 0, 0, 0};
+          R.s[p * NR + rr][m] = 0.f;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2 * NR; ++q)
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+      if constexpr (PRE) {
+        chunk_to_bf16<FMT>(raw[q][m], R.w[q][m]);
+      } else {
+        R.w[q][m][0] = raw[q][m][0];
+        R.w[q][m][1] = raw[q][m][1];
+        R.w[q][m][2] = raw[q][m][2];
+        R.w[q][m][3] = raw[q][m][3];
+      }
+    }
+}
+
+template <int FMT, int NR, int MCH, bool PRE, bool XF32>
+__device__ __forceinline__ float gate_chunk_dot(GateRows<FMT, NR, MCH, PRE>& R, int q, int m,
+                                                const XChunk<FMT, XF32>& xc) {
+  if constexpr (PRE) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < GateRows<FMT, NR, MCH, PRE>::kWords; ++i)
+      acc = dot2_bf16(as_bf16x2(R.w[q][m][i]), as_bf16x2(xc.v[i]), acc);
+    return acc;
+  } else {
+    u32x4 w = {R.w[q][m][0], R.w[q][m][1], R.w[q][m][2], R.w[q][m][3]};
+    opaque(w);   // keep the conversion per token (registers), see PRE
+    return chunk_dot<FMT, XF32>(w, xc);
+  }
+}
+
+// All MCH activation chunks of one token are requested before any is used.
+template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD>
+__device__ __forceinline__ void gate_up_pair(GateRows<FMT, NR, MCH, PRE>& R, const GateUpArgs& a,
+                                             int pe, int n0, int lane) {
+  const char* xrow = reinterpret_cast<const char*>(a.x) +
+                     (size_t)div_slots(pe, a.slots_magic) * a.H * (XF32 ? 4 : 2);
+  XChunk<FMT, XF32> xc[MCH];
+#pragma unroll
+  for (int m = 0; m < MCH; ++m) {
+    const int c = lane + m * kWave;
+    load_x_chunk<FMT, XF32>(xc[m], xrow, GUARD ? min(c, a.chunks - 1) : c);
+  }
+  float acc[2 * NR];
+#pragma unroll
+  for (int q = 0; q < 2 * NR; ++q) {
+    acc[q] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MCH; ++m)
+      acc[q] = fmaf(gate_chunk_dot<FMT, NR, MCH, PRE, XF32>(R, q, m, xc[m]), R.s[q][m], acc[q]);
+  }
+  float out;
+  if constexpr (NR == 2) {
+    const float r = wave_sum4_rows(acc[0], acc[1], acc[2], acc[3]);
+    const float g0 = lane_value(r, 0), g1 = lane_value(r, 16);
+    const float u0 = lane_value(r, 32), u1 = lane_value(r, 48);
+    out = lane == 0 ? swiglu(g0, u0) : swiglu(g1, u1);
+  } else {
+    const float r = wave_sum2_halves(acc[0], acc[1]);
+    out = swiglu(lane_value(r, 0), lane_value(r, 32));
+  }
+  if (lane < NR && n0 + lane < a.I) {
+    const size_t off = (size_t)pe * a.I + n0 + lane;
+    if constexpr (HBF16) {
+      reinterpret_cast<uint16_t*>(a.h)[off] = (uint16_t)f32_to_bf16_bits(out);
+    } else {
+      reinterpret_cast<float*>(a.h)[off] = out;
+    }
+  }
+}
+
+template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD>
+MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs a) {
   __shared__ int s_ids[kDecodeMaxEntries];
   __shared__ uint32_t s_mask[kMaskWords];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int n_exp = a.E + (a.slots - a.k);
-
-  for (int q = tid; q < a.n_words; q += kBlock) s_mask[q] = 0;
-  __syncthreads();
-  for (int v = tid; v < a.n_entries; v += kBlock) {
-    const int t = v / a.slots, j = v - t * a.slots;
-    const int e = j < a.k ? clamp_expert(a.ids[t * a.k + j], a.E) : a.E;
-    s_ids[v] = e;
-    atomicOr(&s_mask[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-
-  int U = 0;
-  for (int q = 0; q < a.n_words; ++q) U += __popc(s_mask[q]);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
   const int n_items = U * a.n_groups;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  constexpr int EPC = Chunk<FMT>::kElems;
-  (void)n_exp;
-
-  for (int it = blockIdx.x * kWavesPerBlock + (tid >> 6); it < n_items; it += n_waves) {
-    const int r = it / a.n_groups;
-    const int g = it - r * a.n_groups;
-    const int e = select_rank(s_mask, a.n_words, r);
-    const int n0 = g * NR;
-
-    // gate rows [0, NR), up rows [NR, 2NR): load every chunk of the lane once
-    u32x4 wv[2 * NR][MCH];
-    float sc[2 * NR][MCH];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int rr = 0; rr < NR; ++rr) {
-        const int n = min(n0 + rr, a.I - 1);
-        const long long row = ((long long)e * 2 + p) * a.I + n;
-        const long long tile_row = ((long long)e * 2 + p) * (a.I >> 7) + (n >> 7);
-        const uint8_t* base = a.w13 + row * a.row_bytes;
-#pragma unroll
-        for (int m = 0; m < MCH; ++m) {
-          const int c = lane + m * kWave;
-          if (c < a.chunks) {
-            wv[p * NR + rr][m] = load_stream16(base + (size_t)c * 16);
-            sc[p * NR + rr][m] = chunk_scale<FMT>(a.w13s, row, c,
-                                                  FMT == W_FP8B128 ? (a.H >> 7) : (a.H >> 5),
-                                                  tile_row);
-          } else {
-            wv[p * NR + rr][m] = u32x4{0, 0, 0, 0};
-            sc[p * NR + rr][m] = 0.f;
-          }
-        }
-      }
-    }
-
-    for (int base = 0; base < a.n_entries; base += kWave) {
-      const int v = base + lane;
-      const bool hit = v < a.n_entries && s_ids[v] == e;
-      unsigned long long bm = __ballot(hit);
-      while (bm) {
-        const int b = __ffsll((long long)bm) - 1;
-        bm &= bm - 1;
-        const int pe = base + b;                    // entry index = t*slots + j
-        const int t = pe / a.slots;
-        const char* xrow = reinterpret_cast<const char*>(a.x) +
-                           (size_t)t * a.H * (XF32 ? 4 : 2);
-        float acc[2 * NR];
-#pragma unroll
-        for (int q = 0; q < 2 * NR; ++q) acc[q] = 0.f;
-#pragma unroll
-        for (int m = 0; m < MCH; ++m) {
-          const int c = lane + m * kWave;
-          if (c < a.chunks) {
-            XChunk<FMT, XF32> xc;
-            load_x_chunk<FMT, XF32>(xc, xrow, c);
-#pragma unroll
-            for (int q = 0; q < 2 * NR; ++q)
-              acc[q] = fmaf(chunk_dot<FMT, XF32>(wv[q][m], xc), sc[q][m], acc[q]);
-          }
-        }
-        float out = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < NR; ++rr) {
-          const float gsum = wave_sum(acc[rr]);
-          const float usum = wave_sum(acc[NR + rr]);
-          if (lane == rr) out = swiglu(gsum, usum);
-        }
-        if (lane < NR && n0 + lane < a.I) {
-          const size_t off = (size_t)pe * a.I + n0 + lane;
-          if constexpr (HBF16) {
-            reinterpret_cast<uint16_t*>(a.h)[off] = (uint16_t)f32_to_bf16_bits(out);
-          } else {
-            reinterpret_cast<float*>(a.h)[off] = out;
-          }
-        }
-      }
-    }
+  for (int it = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); it < n_items; it += n_waves) {
+    const int e = select_rank(s_mask, a.n_words, it / a.n_groups);
+    const int n0 = (it % a.n_groups) * NR;
+    GateRows<FMT, NR, MCH, PRE> rows;
+    load_gate_rows<FMT, NR, MCH, PRE, GUARD>(rows, a, e, n0, lane);
+    PairIter pi;
+    pairs_begin(pi, s_ids, a.n_entries, e);
+    for (int pe = pairs_next(pi, s_ids, a.n_entries, e); pe >= 0;
+         pe = pairs_next(pi, s_ids, a.n_entries, e))
+      gate_up_pair<FMT, NR, MCH, PRE, XF32, HBF16, GUARD>(rows, a, pe, n0, lane);
   }
-  (void)EPC;
 }
 
-// h chunk matching w2 chunk c of slot j: Chunk<FMT>::kElems elements.
-template <int FMT, bool HBF16>
-using HChunk = XChunk<FMT, !HBF16>;
+// ---------------------------------------------------------------------------
+// down: shared per-row dot product over LPR lanes
+// ---------------------------------------------------------------------------
 
-template <int FMT, int ND, bool HBF16, bool YBF16>
-__global__ __launch_bounds__(kBlock) void down_decode_kernel(const DownArgs a) {
+template <int FMT, int CPL>
+struct DownRow {
+  u32x4 w[CPL];
+  float s[CPL];
+};
+
+template <int FMT, int LPR, int CPL>
+__device__ __forceinline__ void load_down_row(DownRow<FMT, CPL>& R, const DownArgs& a, int e,
+                                              int d, int gl, bool stream) {
+  const long long row = (long long)e * a.H + d;
+  const long long tile_row = (long long)e * (a.H >> 7) + (d >> 7);
+  const uint8_t* base = a.w2 + row * a.row_bytes;
+  const int scale_len = FMT == W_FP8B128 ? (a.I >> 7) : (a.I >> 5);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = gl + LPR * i;
+    R.w[i] = stream ? load_stream16(base + (size_t)c * 16) : load16(base + (size_t)c * 16);
+    R.s[i] = chunk_scale<FMT>(a.w2s, row, c, scale_len, tile_row);
+  }
+}
+
+// dot(row r, h[pe]) for the lane's RPL rows, each reduced over its LPR lanes
+// (every lane of the group gets the totals).  Fixed order per row: chunk by
+// chunk per lane, then the DPP tree; the staged h chunks serve all RPL rows.
+template <int FMT, int LPR, int CPL, int RPL, bool HBF16>
+__device__ __forceinline__ void down_rows_dot(DownRow<FMT, CPL> (&R)[RPL], const DownArgs& a,
+                                              int pe, int gl, float (&out)[RPL]) {
+  const size_t h_row_bytes = (size_t)a.I * (HBF16 ? 2 : 4);
+  const char* hrow = reinterpret_cast<const char*>(a.h) + (size_t)pe * h_row_bytes;
+  XChunk<FMT, !HBF16> hc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) load_x_chunk<FMT, !HBF16>(hc[i], hrow, gl + LPR * i);
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) opaque(R[r].w[i]);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      acc = fmaf(chunk_dot<FMT, !HBF16>(R[r].w[i], hc[i]), R[r].s[i], acc);
+    if constexpr (LPR == 32) out[r] = half32_sum(acc);
+    else if constexpr (LPR == 16) out[r] = row16_sum(acc);
+    else if constexpr (LPR == 8) out[r] = group8_sum(acc);
+    else out[r] = group4_sum(acc);
+  }
+}
+
+__device__ __forceinline__ float slot_weight(const DownArgs& a, int pe) {
+  const int t = div_slots(pe, a.slots_magic), j = pe - t * a.slots;
+  return j < a.k ? a.wts[t * a.k + j] : 1.0f;
+}
+
+// VGPRs the staged h chunks of one lane take.
+template <int FMT, int CPL, bool HBF16>
+constexpr int h_regs() { return CPL * Chunk<FMT>::kElems * (HBF16 ? 2 : 4) / 4; }
+
+// Expert-major: slot_out[pe][d] = w_pe * dot(Wd[e][d], h[pe]).  A wavefront
+// item is RPL * 64/LPR output rows of one expert.
+template <int FMT, int LPR, int CPL, int RPL, bool HBF16>
+MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void down_expert_kernel(
+    const DownArgs a) {
+  __shared__ int s_ids[kDecodeMaxEntries];
+  __shared__ uint32_t s_mask[kMaskWords];
+  constexpr int ND = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x, a.nxcd);
-  const int item = lb * kWavesPerBlock + (threadIdx.x >> 6);
-  if (item >= a.T * a.n_dgroups) return;
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
+  const int n_items = U * a.n_dgroups;
+  const int n_waves = gridDim.x * kWavesPerBlock;
+  float* out = reinterpret_cast<float*>(a.y);
+  for (int it = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); it < n_items; it += n_waves) {
+    const int e = select_rank(s_mask, a.n_words, it / a.n_dgroups);
+    const int d0 = (it % a.n_dgroups) * ND * RPL + grp;
+    DownRow<FMT, CPL> rows[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      load_down_row<FMT, LPR, CPL>(rows[r], a, e, min(d0 + r * ND, a.H - 1), gl, true);
+    PairIter pi;
+    pairs_begin(pi, s_ids, a.n_entries, e);
+    for (int pe = pairs_next(pi, s_ids, a.n_entries, e); pe >= 0;
+         pe = pairs_next(pi, s_ids, a.n_entries, e)) {
+      float dot[RPL];
+      down_rows_dot<FMT, LPR, CPL, RPL, HBF16>(rows, a, pe, gl, dot);
+      const float w = slot_weight(a, pe);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+        if (gl == 0 && d0 + r * ND < a.H)
+          out[(size_t)pe * a.H + d0 + r * ND] = __fmul_rn(dot[r], w);
+    }
+  }
+}
+
+// Token-major: y[t][d] = sum over slots j (in order) of w_tj * dot(Wd[e_tj][d], h[t][j]).
+// A workgroup owns one (token, output group); its 4 wavefronts take the slots
+// j = w, w+4, ... and park w * dot in LDS; wavefront 0 adds them in slot order.
+template <int FMT, int LPR, int CPL, bool HBF16, bool YBF16>
+MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void down_token_kernel(const DownArgs a) {
+  constexpr int ND = kWave / LPR;
+  __shared__ float s_part[64][ND];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int item = xcd_logical_block(blockIdx.x, gridDim.x, a.nxcd);
   const int dg = item / a.T;
   const int t = item - dg * a.T;
-  const int d0 = dg * ND;
+  const int d = dg * ND + grp;   // token-major items are one row per lane group
+  const int dd = min(d, a.H - 1);
 
   int my_e = 0;
   float my_w = 0.f;
@@ -262,49 +481,22 @@ __global__ __launch_bounds__(kBlock) void down_decode_kernel(const DownArgs a) {
       my_w = 1.0f;
     }
   }
-
-  float acc[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) acc[d] = 0.f;
-
-  const int n_m = (a.F + kWave - 1) / kWave;
-  const size_t h_row_bytes = (size_t)a.I * (HBF16 ? 2 : 4);
-  const char* hbase = reinterpret_cast<const char*>(a.h) + (size_t)t * a.slots * h_row_bytes;
-  const int scale_len = FMT == W_FP8B128 ? (a.I >> 7) : (a.I >> 5);
-  for (int m = 0; m < n_m; ++m) {
-    const int f = m * kWave + lane;
-    const bool valid = f < a.F;
-    const int fj = valid ? f / a.chunks : 0;
-    const int c = valid ? f - fj * a.chunks : 0;
-    const int e = __shfl(my_e, fj);
-    const float w = __shfl(my_w, fj);
-    if (valid) {
-      HChunk<FMT, HBF16> hc;
-      load_x_chunk<FMT, !HBF16>(hc, hbase + (size_t)fj * h_row_bytes, c);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const int dd = min(d0 + d, a.H - 1);
-        const long long row = (long long)e * a.H + dd;
-        const long long tile_row = (long long)e * (a.H >> 7) + (dd >> 7);
-        const u32x4 wq = load16(a.w2 + row * a.row_bytes + (size_t)c * 16);
-        const float s = chunk_scale<FMT>(a.w2s, row, c, scale_len, tile_row);
-        acc[d] = fmaf(chunk_dot<FMT, !HBF16>(wq, hc), s * w, acc[d]);
-      }
-    }
+  for (int j = wv; j < a.slots; j += kWavesPerBlock) {
+    DownRow<FMT, CPL> R[1];
+    load_down_row<FMT, LPR, CPL>(R[0], a, __builtin_amdgcn_readlane(my_e, j), dd, gl, false);
+    float dot[1];
+    down_rows_dot<FMT, LPR, CPL, 1, HBF16>(R, a, t * a.slots + j, gl, dot);
+    if (gl == 0) s_part[j][grp] = __fmul_rn(dot[0], lane_value(my_w, j));
   }
-
-  float out = 0.f;
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const float v = wave_sum(acc[d]);
-    if (lane == d) out = v;
-  }
-  if (lane < ND && d0 + lane < a.H) {
-    const size_t off = (size_t)t * a.H + d0 + lane;
+  __syncthreads();
+  if (wv == 0 && gl == 0 && d < a.H) {
+    float y = 0.f;
+    for (int j = 0; j < a.slots; ++j) y = __fadd_rn(y, s_part[j][grp]);
+    const size_t off = (size_t)t * a.H + d;
     if constexpr (YBF16) {
-      reinterpret_cast<uint16_t*>(a.y)[off] = (uint16_t)f32_to_bf16_bits(out);
+      reinterpret_cast<uint16_t*>(a.y)[off] = (uint16_t)f32_to_bf16_bits(y);
     } else {
-      reinterpret_cast<float*>(a.y)[off] = out;
+      reinterpret_cast<float*>(a.y)[off] = y;
     }
   }
 }
@@ -317,43 +509,89 @@ int row_bytes_of(int fmt, int k_elems) {
   }
 }
 
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v ? std::atoi(v) : dflt;
+}
+
 // ---- dispatch ------------------------------------------------------------
 
-template <int FMT, int NR, bool XF32, bool HBF16>
-hipError_t gate_up_mch(const GateUpArgs& a, int mch, int blocks, hipStream_t s) {
+template <int FMT, int NR, bool PRE, bool XF32, bool HBF16>
+hipError_t gate_up_mch(const GateUpArgs& a, int mch, bool guard, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
-  switch (mch) {
-    case 1: hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, 1, XF32, HBF16>), g, b, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, 2, XF32, HBF16>), g, b, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, 4, XF32, HBF16>), g, b, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, 8, XF32, HBF16>), g, b, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+#define MOE_GU(M, G) \
+  hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G>), g, b, 0, s, a)
+  if (!guard) {
+    switch (mch) {
+      case 1: MOE_GU(1, false); break;
+      case 2: MOE_GU(2, false); break;
+      case 4: MOE_GU(4, false); break;
+      case 7: MOE_GU(7, false); break;
+      case 8: MOE_GU(8, false); break;
+      default: return hipErrorNotSupported;
+    }
+  } else {
+    switch (mch) {
+      case 1: MOE_GU(1, true); break;
+      case 2: MOE_GU(2, true); break;
+      case 4: MOE_GU(4, true); break;
+      case 8: MOE_GU(8, true); break;
+      default: return hipErrorNotSupported;
+    }
   }
+#undef MOE_GU
   return hipGetLastError();
 }
 
 template <int FMT, bool XF32, bool HBF16>
-hipError_t gate_up_nr(const GateUpArgs& a, int nr, int mch, int blocks, hipStream_t s) {
-  if (nr == 1) return gate_up_mch<FMT, 1, XF32, HBF16>(a, mch, blocks, s);
-  return gate_up_mch<FMT, 2, XF32, HBF16>(a, mch, blocks, s);
+hipError_t gate_up_nr(const GateUpArgs& a, int nr, bool pre, int mch, bool guard, int blocks,
+                      hipStream_t s) {
+  if constexpr (FMT == W_F32) {
+    if (nr == 1) return gate_up_mch<FMT, 1, false, XF32, HBF16>(a, mch, guard, blocks, s);
+    return gate_up_mch<FMT, 2, false, XF32, HBF16>(a, mch, guard, blocks, s);
+  } else {
+    if (nr == 1)
+      return pre ? gate_up_mch<FMT, 1, true, XF32, HBF16>(a, mch, guard, blocks, s)
+                 : gate_up_mch<FMT, 1, false, XF32, HBF16>(a, mch, guard, blocks, s);
+    return pre ? gate_up_mch<FMT, 2, true, XF32, HBF16>(a, mch, guard, blocks, s)
+               : gate_up_mch<FMT, 2, false, XF32, HBF16>(a, mch, guard, blocks, s);
+  }
 }
 
-template <int FMT, int ND, bool HBF16>
-hipError_t down_y(const DownArgs& a, int ybf16, int blocks, hipStream_t s) {
+template <int FMT, int LPR, int CPL, bool HBF16>
+hipError_t down_launch(const DownArgs& a, bool expert_major, int ybf16, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
-  if (ybf16) hipLaunchKernelGGL((down_decode_kernel<FMT, ND, HBF16, true>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((down_decode_kernel<FMT, ND, HBF16, false>), g, b, 0, s, a);
+  if (expert_major && a.rpl == 2)
+    hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 2, HBF16>), g, b, 0, s, a);
+  else if (expert_major)
+    hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 1, HBF16>), g, b, 0, s, a);
+  else if (ybf16)
+    hipLaunchKernelGGL((down_token_kernel<FMT, LPR, CPL, HBF16, true>), g, b, 0, s, a);
+  else
+    hipLaunchKernelGGL((down_token_kernel<FMT, LPR, CPL, HBF16, false>), g, b, 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, bool HBF16>
-hipError_t down_nd(const DownArgs& a, int nd, int ybf16, int blocks, hipStream_t s) {
-  switch (nd) {
-    case 1: return down_y<FMT, 1, HBF16>(a, ybf16, blocks, s);
-    case 2: return down_y<FMT, 2, HBF16>(a, ybf16, blocks, s);
-    case 4: return down_y<FMT, 4, HBF16>(a, ybf16, blocks, s);
-    default: return down_y<FMT, 8, HBF16>(a, ybf16, blocks, s);
+template <int FMT, int LPR, bool HBF16>
+hipError_t down_cpl(const DownArgs& a, bool em, int ybf16, int blocks, hipStream_t s) {
+  switch (a.cpl) {
+    case 2: return down_launch<FMT, LPR, 2, HBF16>(a, em, ybf16, blocks, s);
+    case 3: return down_launch<FMT, LPR, 3, HBF16>(a, em, ybf16, blocks, s);
+    case 4: return down_launch<FMT, LPR, 4, HBF16>(a, em, ybf16, blocks, s);
+    case 6: return down_launch<FMT, LPR, 6, HBF16>(a, em, ybf16, blocks, s);
+    case 8: return down_launch<FMT, LPR, 8, HBF16>(a, em, ybf16, blocks, s);
+    case 12: return down_launch<FMT, LPR, 12, HBF16>(a, em, ybf16, blocks, s);
+    case 16: return down_launch<FMT, LPR, 16, HBF16>(a, em, ybf16, blocks, s);
+    default: return hipErrorNotSupported;
   }
+}
+
+template <int FMT, bool HBF16>
+hipError_t down_shape(const DownArgs& a, int lpr, bool em, int ybf16, int blocks, hipStream_t s) {
+  if (lpr == 4) return down_cpl<FMT, 4, HBF16>(a, em, ybf16, blocks, s);
+  if (lpr == 8) return down_cpl<FMT, 8, HBF16>(a, em, ybf16, blocks, s);
+  if (lpr == 16) return down_cpl<FMT, 16, HBF16>(a, em, ybf16, blocks, s);
+  return down_cpl<FMT, 32, HBF16>(a, em, ybf16, blocks, s);
 }
 
 }  // namespace
@@ -378,48 +616,87 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
   a.n_entries = T * a.slots;
-  // wider neuron groups amortise the activation reads; one row pair when a
-  // lane already holds many chunks of a long row
+  // chunks per lane: exact when the row is a whole number of 64-lane passes
+  // (loads then batch without guards), else the next instantiated size
   const int lane_chunks = (a.chunks + kWave - 1) / kWave;
-  const int mch = lane_chunks <= 1 ? 1 : lane_chunks <= 2 ? 2 : lane_chunks <= 4 ? 4 : 8;
-  const int nr = mch >= 8 ? 1 : 2;
+  const bool guard = a.chunks % kWave != 0 ||
+                     !(lane_chunks == 1 || lane_chunks == 2 || lane_chunks == 4 ||
+                       lane_chunks == 7 || lane_chunks == 8);
+  const int mch = !guard ? lane_chunks
+                         : lane_chunks <= 1 ? 1 : lane_chunks <= 2 ? 2 : lane_chunks <= 4 ? 4 : 8;
+  if (lane_chunks > 8) return hipErrorNotSupported;
+  // neurons per wavefront: two while the rows stay small in registers; rows
+  // converted to BF16 once per item while that takes at most 64 VGPRs
+  const int nr = env_int("MOE_TUNE_GU_NR", mch <= 2 ? 2 : 1);
+  const int elems = W.format == W_MXFP4 ? 32 : 16;
+  const bool pre = W.format != W_F32 &&
+                   env_int("MOE_TUNE_GU_PRE", 2 * nr * mch * elems / 2 <= 64 ? 1 : 0) != 0;
+  a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
   a.n_groups = (W.inter + nr - 1) / nr;
   const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_groups;
   const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int cap = device_num_cus() * 4;
+  const int cap = device_num_cus() * env_int("MOE_TUNE_GU_BPC", 16);
   const int blocks = (int)std::max<long long>(1, std::min<long long>(want, cap));
   const bool xf32 = x_dtype == MOE_DT_F32;
   const bool hbf = h_dtype == MOE_DT_BF16;
   switch (W.format) {
     case W_F32:
-      if (xf32) return hbf ? gate_up_nr<W_F32, true, true>(a, nr, mch, blocks, s)
-                           : gate_up_nr<W_F32, true, false>(a, nr, mch, blocks, s);
-      return hbf ? gate_up_nr<W_F32, false, true>(a, nr, mch, blocks, s)
-                 : gate_up_nr<W_F32, false, false>(a, nr, mch, blocks, s);
+      if (xf32) return hbf ? gate_up_nr<W_F32, true, true>(a, nr, pre, mch, guard, blocks, s)
+                           : gate_up_nr<W_F32, true, false>(a, nr, pre, mch, guard, blocks, s);
+      return hbf ? gate_up_nr<W_F32, false, true>(a, nr, pre, mch, guard, blocks, s)
+                 : gate_up_nr<W_F32, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_MXFP8:
-      return hbf ? gate_up_nr<W_MXFP8, false, true>(a, nr, mch, blocks, s)
-                 : gate_up_nr<W_MXFP8, false, false>(a, nr, mch, blocks, s);
+      return hbf ? gate_up_nr<W_MXFP8, false, true>(a, nr, pre, mch, guard, blocks, s)
+                 : gate_up_nr<W_MXFP8, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_MXFP4:
-      return hbf ? gate_up_nr<W_MXFP4, false, true>(a, nr, mch, blocks, s)
-                 : gate_up_nr<W_MXFP4, false, false>(a, nr, mch, blocks, s);
+      return hbf ? gate_up_nr<W_MXFP4, false, true>(a, nr, pre, mch, guard, blocks, s)
+                 : gate_up_nr<W_MXFP4, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_FP8B128:
-      return hbf ? gate_up_nr<W_FP8B128, false, true>(a, nr, mch, blocks, s)
-                 : gate_up_nr<W_FP8B128, false, false>(a, nr, mch, blocks, s);
+      return hbf ? gate_up_nr<W_FP8B128, false, true>(a, nr, pre, mch, guard, blocks, s)
+                 : gate_up_nr<W_FP8B128, false, false>(a, nr, pre, mch, guard, blocks, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
+// Lanes that share one W_down row.  It depends only on the format, the row
+// length and the h dtype (both down variants use it, so their bits agree):
+// the fewest lanes such that the row splits into an instantiated number of
+// chunks per lane and two rows per lane group fit the register budget
+// (weights + scales ~5 VGPRs per chunk, plus the staged h chunks); failing
+// that, one row per group with at most 48 (then 96) VGPRs of h.  0 if none.
+int down_lanes_per_row(int fmt, int inter, int h_dtype) {
+  const int chunks = row_bytes_of(fmt, inter) / 16;
+  const int elems = fmt == W_F32 ? 4 : fmt == W_MXFP4 ? 32 : 16;
+  const int hwords = elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
+  auto inst = [&](int lpr) {
+    if (chunks % lpr) return false;
+    const int c = chunks / lpr;
+    return c == 2 || c == 3 || c == 4 || c == 6 || c == 8 || c == 12 || c == 16;
+  };
+  const int forced = env_int("MOE_TUNE_DN_LPR", 0);
+  if (forced && inst(forced)) return forced;
+  for (int lpr : {4, 8, 16, 32}) {
+    const int c = chunks / lpr;
+    if (inst(lpr) && (lpr >= 8 || chunks < 16) && 2 * c * 5 + c * hwords <= 80) return lpr;
+  }
+  for (int budget = 48; budget <= 128; budget *= 2)
+    for (int lpr : {4, 8, 16, 32})
+      if (inst(lpr) && (lpr >= 8 || chunks < 16) && (chunks / lpr) * hwords <= budget) return lpr;
+  return 0;
+}
+
+bool down_expert_major(int T) { return T >= env_int("MOE_TUNE_DN_EM_MIN_T", 4); }
+
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               const int32_t* ids, const float* wts, int T, int k, void* y,
-                              int y_dtype, hipStream_t s) {
+                              int y_dtype, float* slot_out, hipStream_t s) {
   DownArgs a;
   a.w2 = reinterpret_cast<const uint8_t*>(W.w2);
   a.w2s = W.w2_scale;
   a.h = h;
   a.ids = ids;
   a.wts = wts;
-  a.y = y;
   a.T = T;
   a.k = k;
   a.slots = k + W.num_shared;
@@ -428,30 +705,59 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
   a.I = W.inter;
   a.row_bytes = row_bytes_of(W.format, W.inter);
   a.chunks = a.row_bytes / 16;
-  a.F = a.slots * a.chunks;
+  const int lpr = down_lanes_per_row(W.format, W.inter, h_dtype);
+  if (lpr == 0) return hipErrorNotSupported;
+  a.cpl = a.chunks / lpr;
+  const int nd = kWave / lpr;
+  a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
+  const bool em_launch = slot_out != nullptr;
+  // two rows per lane group in the expert-major kernel: twice the bytes per
+  // item, each staged h chunk used twice
+  const int elems = W.format == W_F32 ? 4 : W.format == W_MXFP4 ? 32 : 16;
+  const int hregs = a.cpl * elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
+  a.rpl = em_launch ? env_int("MOE_TUNE_DN_RPL", 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1) : 1;
+  a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
+  const int n_exp = W.num_experts + W.num_shared;
+  a.n_words = (n_exp + 31) / 32;
+  a.n_entries = T * a.slots;
   a.nxcd = device_num_xcds();
-  // output rows per wave: enough waves to fill the chip at small T, more
-  // reuse of the staged h chunk at large T
-  const long long target_waves = (long long)device_num_cus() * 8;
-  int nd = 8;
-  while (nd > 1 && (long long)T * ((W.hidden + nd - 1) / nd) < target_waves) nd >>= 1;
-  a.n_dgroups = (W.hidden + nd - 1) / nd;
-  const long long items = (long long)T * a.n_dgroups;
-  const int blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
   const bool hbf = h_dtype == MOE_DT_BF16;
   const int ybf = y_dtype == MOE_DT_BF16;
+  const bool em = slot_out != nullptr;
+  int blocks;
+  if (em) {
+    a.y = slot_out;
+    const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_dgroups;
+    const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int cap = device_num_cus() * env_int("MOE_TUNE_DN_BPC", 8);
+    blocks = (int)std::max<long long>(1, std::min<long long>(want, cap));
+  } else {
+    a.y = y;
+    blocks = T * a.n_dgroups;              // one workgroup per (token, output group)
+  }
+  hipError_t err;
   switch (W.format) {
     case W_F32:
-      return hbf ? down_nd<W_F32, true>(a, nd, ybf, blocks, s) : down_nd<W_F32, false>(a, nd, ybf, blocks, s);
+      err = hbf ? down_shape<W_F32, true>(a, lpr, em, ybf, blocks, s)
+                : down_shape<W_F32, false>(a, lpr, em, ybf, blocks, s);
+      break;
     case W_MXFP8:
-      return hbf ? down_nd<W_MXFP8, true>(a, nd, ybf, blocks, s) : down_nd<W_MXFP8, false>(a, nd, ybf, blocks, s);
+      err = hbf ? down_shape<W_MXFP8, true>(a, lpr, em, ybf, blocks, s)
+                : down_shape<W_MXFP8, false>(a, lpr, em, ybf, blocks, s);
+      break;
     case W_MXFP4:
-      return hbf ? down_nd<W_MXFP4, true>(a, nd, ybf, blocks, s) : down_nd<W_MXFP4, false>(a, nd, ybf, blocks, s);
+      err = hbf ? down_shape<W_MXFP4, true>(a, lpr, em, ybf, blocks, s)
+                : down_shape<W_MXFP4, false>(a, lpr, em, ybf, blocks, s);
+      break;
     case W_FP8B128:
-      return hbf ? down_nd<W_FP8B128, true>(a, nd, ybf, blocks, s) : down_nd<W_FP8B128, false>(a, nd, ybf, blocks, s);
+      err = hbf ? down_shape<W_FP8B128, true>(a, lpr, em, ybf, blocks, s)
+                : down_shape<W_FP8B128, false>(a, lpr, em, ybf, blocks, s);
+      break;
     default:
       return hipErrorInvalidValue;
   }
+  if (err != hipSuccess || !em) return err;
+  return launch_combine(slot_out, T, a.slots, W.hidden, y, y_dtype, s);
 }
 
 }  // namespace moe

@@ -28,6 +28,15 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Empty register barrier: the compiler must assume v changed here.  Used on
+// weight registers inside per-token loops so the format conversion is redone
+// per token (a few VALU ops) instead of being hoisted into 2-4x more registers.
+__device__ __forceinline__ void opaque(u32x4& v) {
+  uint32_t a = v[0], b = v[1], c = v[2], d = v[3];
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  v = u32x4{a, b, c, d};
+}
+
 // ---------------------------------------------------------------------------
 // number formats
 // ---------------------------------------------------------------------------
@@ -165,17 +174,71 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
+// Sum over the 16 lanes of each DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<0x128>(x);  // row_ror:8
   x += dpp_f32<0x124>(x);  // row_ror:4
   x += dpp_f32<0x122>(x);  // row_ror:2
   x += dpp_f32<0x121>(x);  // row_ror:1
+  return x;
+}
+
+// Sum over each half wave (two DPP rows); every lane of the half gets it.
+__device__ __forceinline__ float half32_sum(float x) {
+  x = row16_sum(x);
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over each aligned group of 8 lanes (half a DPP row).
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_f32<0x141>(x);  // row_half_mirror: lane i <- 7 - i within the half row
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+
+// Sum over each aligned group of 4 lanes (a DPP quad).
+__device__ __forceinline__ float group4_sum(float x) {
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
   uint32_t u = __float_as_uint(x);
   auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
   u = __float_as_uint(x);
   auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Four wave sums at once: on return DPP row 0 holds sum(a), row 1 sum(b),
+// row 2 sum(c), row 3 sum(d) (every lane of the row).  The halves are folded
+// with permlane32 swaps (a with c, b with d), the row pairs with a
+// permlane16 swap, then each row is finished with DPP rotations.
+__device__ __forceinline__ float wave_sum4_rows(float a, float b, float c, float d) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
+  const float u = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // lo: a, hi: c
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(b), __float_as_uint(d), false, false);
+  const float v = __uint_as_float(q[0]) + __uint_as_float(q[1]);   // lo: b, hi: d
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return row16_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// Two wave sums at once: rows 0-1 hold sum(a), rows 2-3 sum(b).
+__device__ __forceinline__ float wave_sum2_halves(float a, float b) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float u = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // lo: a, hi: b
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+  return row16_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -20,9 +20,13 @@ int device_num_xcds();
 hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
                                  const int32_t* ids, int T, int k, void* h, int h_dtype,
                                  hipStream_t s);
+// slot_out (T*slots*H floats) selects the expert-major variant + combine;
+// nullptr runs the token-major variant.  Both give identical bits.
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               const int32_t* ids, const float* wts, int T, int k, void* y,
-                              int y_dtype, hipStream_t s);
+                              int y_dtype, float* slot_out, hipStream_t s);
+int down_lanes_per_row(int fmt, int inter, int h_dtype);
+bool down_expert_major(int T);
 
 // align_sort.hip
 size_t align_sort_workspace_bytes(int n_entries, int n_experts);

@@ -80,14 +80,18 @@ def test_host_argument_errors(lib):
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 0, dummy, 4, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
     # misaligned weight pointer, bad format, non-multiple-of-32 hidden
     assert lib.moe_down(ctypes.byref(_weights(moe, w13=17)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
-                        None) == moe.ERR_INVALID_ARG
+                        None, 0, None) == moe.ERR_INVALID_ARG
     assert lib.moe_down(ctypes.byref(_weights(moe, format=9)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
-                        None) == moe.ERR_INVALID_ARG
+                        None, 0, None) == moe.ERR_INVALID_ARG
     assert lib.moe_down(ctypes.byref(_weights(moe, hidden=2050)), dummy, 0, dummy, dummy, 4, 8, dummy,
-                        0, None) == moe.ERR_UNSUPPORTED
+                        0, None, 0, None) == moe.ERR_UNSUPPORTED
     # missing scales for a quantised format
     assert lib.moe_down(ctypes.byref(_weights(moe, w2_scale=None)), dummy, 0, dummy, dummy, 4, 8, dummy,
-                        0, None) == moe.ERR_INVALID_ARG
+                        0, None, 0, None) == moe.ERR_INVALID_ARG
+    # workspace given but too small
+    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, dummy, 64,
+                        None) == moe.ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_down_workspace_bytes(ctypes.byref(w), 4, 8) == 4 * 8 * 2048 * 4
     # T == 0 is a no-op
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 0, 8, dummy, 0, None) == moe.OK
     # align-sort: block size, workspace
@@ -118,7 +122,7 @@ def test_path_choice_host_logic(lib):
     # fp32 weights have no grouped path
     w32 = _weights(__import__("mixture_experts_decode_amd"), format=0)
     assert lib.moe_choose_path(ctypes.byref(w32), 16384, 8) == DEC
-    # workspace sizes: decode = T*slots*I*4 rounded up to 256
-    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * 768 * 4
+    # workspace sizes: decode = h (T*slots*I, BF16) + slot outputs (T*slots*H*4)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * (768 * 2 + 2048 * 4)
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 64) > 0
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 48) == 0

@@ -98,9 +98,27 @@ def test_batch_invariance_and_determinism(lib):
     assert torch.equal(h_all, h_again) and torch.equal(y_all, y_again)
     for t in (0, 13, 31):
         h1 = lib.gate_up(Wd, xd[t:t + 1].contiguous(), idd[t:t + 1].contiguous())
-        y1 = lib.down(Wd, h1, idd[t:t + 1].contiguous(), wd[t:t + 1].contiguous())
+        y1 = lib.down(Wd, h1, idd[t:t + 1].contiguous(), wd[t:t + 1].contiguous(),
+                      variant="token")
         torch.cuda.synchronize()
         assert torch.equal(h1[0], h_all[t]) and torch.equal(y1[0], y_all[t]), t
+
+
+@pytest.mark.parametrize("fmt", list(SMALL))
+def test_down_variants_bitwise_identical(lib, fmt):
+    """Token-major and expert-major down give the same bits (same per-slot
+    lane groups and reduction tree, slots added in slot order)."""
+    cfg = SMALL[fmt]
+    t = 3 if fmt == "f32" else 13
+    x, ids, w = inputs(cfg, t)
+    Wd = device_weights(cfg)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd)
+    for y_dtype in ("f32", "bf16"):
+        y_tok = lib.down(Wd, h, idd, wd, y_dtype=y_dtype, variant="token")
+        y_exp = lib.down(Wd, h, idd, wd, y_dtype=y_dtype, variant="expert")
+        torch.cuda.synchronize()
+        assert torch.equal(y_tok, y_exp), (fmt, y_dtype)
 
 
 def test_every_output_written(lib):
