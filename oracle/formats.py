@@ -182,3 +182,17 @@ def fake_quant_mx_e4m3(v):
     """Q(v): quantise to MXFP8 and decode back to float64."""
     codes, scales = quantize_mx_e4m3(v)
     return dequant_mx(codes, scales, "e4m3")
+
+
+def quantize_mx_e4m3_two_term(v):
+    """v ~ hi + lo with hi = Q(v) and lo = Q(v - hi): two MXFP8 terms.
+    Returns (codes_hi, scales_hi, codes_lo, scales_lo)."""
+    ch, sh = quantize_mx_e4m3(v)
+    cl, sl = quantize_mx_e4m3(np.asarray(v, dtype=np.float64) - dequant_mx(ch, sh, "e4m3"))
+    return ch, sh, cl, sl
+
+
+def fake_quant_mx_e4m3_two_term(v):
+    """hi + lo decoded back to float64."""
+    ch, sh, cl, sl = quantize_mx_e4m3_two_term(v)
+    return dequant_mx(ch, sh, "e4m3") + dequant_mx(cl, sl, "e4m3")

@@ -21,9 +21,13 @@ Readings (each listed in the design doc):
   reading);
 * ``act_quant="mxfp8"`` models the expert-centric path, whose block-scaled
   matrix cores need 8-bit operands: x_t is MX-quantised per 32 along H before
-  the gate/up products and h_tj per 32 along I before the down product (the
-  align-and-sort article's online FP8 quantisation step in the fused pipeline;
-  the warp-decode post, accuracy section, on this extra rounding).  With
+  the gate/up products (the align-and-sort article's online FP8 quantisation
+  step in the fused pipeline; the warp-decode post, accuracy section, on this
+  extra rounding), and h_tj is requantised per 32 along I (GC-MoE abstract:
+  SwiGLU with requantisation) as two MXFP8 terms, hi = Q(h) and lo = Q(h - hi),
+  both fed to the down product.  A single term would let the matrix core's own
+  accumulation error (about 5e-5 relative on gfx950) flip requantised codes
+  against any exact reference; the second term absorbs such flips.  With
   ``act_quant="none"`` activations stay exact, as on the output-centric path.
 
 All arithmetic is float64.  Experts are dequantised once per call, each only
@@ -147,7 +151,8 @@ def down(h, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert,
     """y [T][H] float64 from a given h [T][k+S][I]: y_t = sum_j w_tj Wd h_tj,
     summed over j in slot order."""
     ids, w = slots(topk_ids, topk_weights, num_experts, num_shared)
-    hh = F.fake_quant_mx_e4m3(h) if act_quant == "mxfp8" else np.asarray(h, dtype=np.float64)
+    hh = (F.fake_quant_mx_e4m3_two_term(h) if act_quant == "mxfp8"
+          else np.asarray(h, dtype=np.float64))
     ys = None
     for e, rows, cols in _group(ids):
         _, _, wd = dequant_expert(fmt, get_expert(e))
@@ -173,7 +178,7 @@ def moe_layer(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_ex
         xa = a[rows]
         hh = silu(xa @ wg.T) * (xa @ wu.T)
         if act_quant == "mxfp8":
-            hh = F.fake_quant_mx_e4m3(hh)
+            hh = F.fake_quant_mx_e4m3_two_term(hh)
         if ys is None:
             ys = np.zeros(ids.shape + (wd.shape[0],))
         ys[rows, cols] = (hh @ wd.T) * w[rows, cols][:, None]
@@ -212,7 +217,7 @@ def moe_layer_scalar(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared,
                 u = math.fsum(wu[n, c] * xt[c] for c in range(n_h))
                 h.append(g / (1.0 + math.exp(-g)) * u)
             if act_quant == "mxfp8":
-                h = [float(v) for v in F.fake_quant_mx_e4m3(np.array(h))]
+                h = [float(v) for v in F.fake_quant_mx_e4m3_two_term(np.array(h))]
             contrib.append([w[t, j] * math.fsum(wd[d, n] * h[n] for n in range(n_i))
                             for d in range(wd.shape[0])])
         rows.append([math.fsum(c[d] for c in contrib) for d in range(len(contrib[0]))])

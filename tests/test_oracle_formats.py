@@ -136,3 +136,27 @@ def test_quantize_mx_block_properties():
     s2 = np.clip(blocks / np.ldexp(1.0, e2.astype(np.int32))[..., None], -448, 448)
     ref = torch.from_numpy(s2.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(codes, ref.reshape(64, 256))
+
+
+def test_two_term_mx_quantisation():
+    """hi = Q(v), lo = Q(v - hi): the second term's block scale follows the
+    residual.  The residual is at most a quarter of the block maximum (when the
+    maximum saturates at 448 scale units; a sixteenth otherwise) and lo keeps
+    it to half an E4M3 step (2^-4), so hi + lo is within 2^-6 of the block
+    maximum; a one-step change of a hi code is absorbed by lo."""
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((32, 256)) * np.exp(rng.uniform(-5, 5, (32, 1)))
+    ch, sh, cl, sl = F.quantize_mx_e4m3_two_term(v)
+    hi = F.dequant_mx(ch, sh, "e4m3")
+    assert np.array_equal(ch, F.quantize_mx_e4m3(v)[0])
+    approx = F.fake_quant_mx_e4m3_two_term(v)
+    bmax = np.repeat(np.abs(v).reshape(32, 8, 32).max(-1), 32, axis=1)
+    assert np.all(np.abs(approx - v) <= bmax * 2.0 ** -6)
+    assert np.median(np.abs(approx - v) / bmax) < 2.0 ** -10
+    # move one hi code by one step: the residual's quantisation compensates
+    ch2 = ch.copy()
+    ch2[0, 5] = ch2[0, 5] + 1 if ch2[0, 5] not in (0x7E, 0xFE) else ch2[0, 5] - 1
+    hi2 = F.dequant_mx(ch2, sh, "e4m3")
+    lo2 = F.fake_quant_mx_e4m3(v - hi2)
+    assert np.abs((hi2 + lo2) - v)[0, :32].max() <= np.abs(v[0, :32]).max() * 2.0 ** -6
+    assert np.abs(hi - v).max() > np.abs(approx - v).max()

@@ -170,13 +170,15 @@ def test_gate_up_then_down_is_the_layer():
 
 
 def test_mxfp8_mode_quantises_activations():
-    """Mode mxfp8 equals mode none run on Q(x) with h replaced by Q(h)."""
+    """Mode mxfp8 equals mode none run on Q(x) with h replaced by its two-term
+    MXFP8 form Q(h) + Q(h - Q(h))."""
     cfg = TINY["mxfp8"]
     x, ids, w = _inputs(cfg, 3)
     kw = _kw(cfg)
     xq = F.fake_quant_mx_e4m3(x)
     h = L.gate_up(xq, ids, **kw)
-    y_ref = L.down(F.fake_quant_mx_e4m3(h), ids, w, **kw)
+    hq = F.fake_quant_mx_e4m3(h)
+    y_ref = L.down(hq + F.fake_quant_mx_e4m3(h - hq), ids, w, **kw)
     assert np.allclose(L.moe_layer(x, ids, w, act_quant="mxfp8", **kw), y_ref, rtol=0, atol=1e-13)
     # and it differs from mode none (the quantisation is really applied)
     assert not np.allclose(L.moe_layer(x, ids, w, **kw), y_ref, rtol=0, atol=1e-6)

@@ -232,6 +232,14 @@ def hidden_states(cfg, t, dtype="f32", variant=0):
     return h if dtype == "f32" else to_bf16_bits(h)
 
 
+def mxfp8_rows(cfg, n, k, variant=0, scale=1.0):
+    """Random MXFP8 activation rows [n][k] (E4M3 codes + E8M0 bytes per 32),
+    encoded from N(0, scale^2) draws; for exercising the grouped GEMMs on
+    their own."""
+    v = rng(cfg, STREAM_H, n, k, variant).standard_normal((n, k), dtype=np.float32)
+    return encode_mxfp8(v * np.float32(scale))
+
+
 def _softmax(z):
     z = z - np.max(z, axis=-1, keepdims=True)
     p = np.exp(z)
