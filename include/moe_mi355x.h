@@ -222,12 +222,15 @@ moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H
 /*
  * moe_grouped_gate_up: for every block b < *num_tokens_post_padded/block_size
  * with expert e = expert_ids[b], G = Xq[b] Wg[e]^T and U = Xq[b] Wu[e]^T on
- * block-scaled MFMA with FP32 accumulation, then h = SiLU(G) * U quantised
- * to MXFP8 per 32 consecutive neurons (the same rule as moe_gather_quant)
- * (GC-MoE abstract: grouped GEMM with SwiGLU and requantisation fused in the
- * epilogue).
+ * block-scaled MFMA with FP32 accumulation, then h = SiLU(G) * U requantised
+ * per 32 consecutive neurons as two MXFP8 terms, hi = Q(h) and
+ * lo = Q(h - hi), with the rule of moe_gather_quant (GC-MoE abstract: grouped
+ * GEMM with SwiGLU and requantisation fused in the epilogue).  The second
+ * term absorbs the code flips a single requantisation would take from the
+ * matrix core's accumulation error.
  *   xq/xs   device, from moe_gather_quant
- *   hq      device [capacity][I] E4M3;  hs device [capacity][I/32] E8M0
+ *   hq      device [2][capacity][I] E4M3 (hi rows, then lo rows)
+ *   hs      device [2][capacity][I/32] E8M0
  * Weight formats: MOE_W_MXFP8, MOE_W_MXFP4, MOE_W_FP8_BLK128.
  * block_size in {32, 64, 128}; H multiple of 128; I multiple of 64.
  */
@@ -237,8 +240,10 @@ moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const ui
                                int32_t block_size, uint8_t* hq, uint8_t* hs, void* stream);
 
 /*
- * moe_grouped_down: for every block b with expert e, O = Hq[b] Wd[e]^T on
- * block-scaled MFMA; row r of O is multiplied by the routing weight of entry
+ * moe_grouped_down: for every block b with expert e, O = (Hhi[b] + Hlo[b]) Wd[e]^T
+ * on block-scaled MFMA (one MFMA per term into the same accumulator), with
+ * hq/hs laid out as moe_grouped_gate_up writes them; row r of O is multiplied
+ * by the routing weight of entry
  * i = sorted_token_ids[r] (1.0 for the shared slot) and stored to
  * slot_out[i][:]; sentinel rows are dropped (warp-decode post, buffer
  * section: the per-expert output buffer of the expert-centric path).

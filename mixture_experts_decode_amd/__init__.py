@@ -227,8 +227,8 @@ def gather_quant(x, slots, sorted_ids, npp, capacity, stream=None):
 
 def grouped_gate_up(W, xq, xs, expert_ids, npp, capacity, block, stream=None):
     load()
-    hq = torch.empty((capacity, W.inter), dtype=torch.uint8, device=xq.device)
-    hs = torch.empty((capacity, W.inter // 32), dtype=torch.uint8, device=xq.device)
+    hq = torch.empty((2, capacity, W.inter), dtype=torch.uint8, device=xq.device)
+    hs = torch.empty((2, capacity, W.inter // 32), dtype=torch.uint8, device=xq.device)
     st = _lib.moe_grouped_gate_up(W.ref, _ptr(xq), _ptr(xs), _ptr(expert_ids), _ptr(npp), capacity,
                                   block, _ptr(hq), _ptr(hs), _stream(stream))
     _check(st, "moe_grouped_gate_up")

@@ -97,8 +97,8 @@ GroupedLayout grouped_layout(const moe_weights* W, int32_t T, int32_t k, int32_t
   L.as_ws = take(moe::align_sort_workspace_bytes(n, n_exp));
   L.xq = take((size_t)L.cap * W->hidden);
   L.xs = take((size_t)L.cap * (W->hidden / 32));
-  L.hq = take((size_t)L.cap * W->inter);
-  L.hs = take((size_t)L.cap * (W->inter / 32));
+  L.hq = take((size_t)2 * L.cap * W->inter);          // hi and lo terms
+  L.hs = take((size_t)2 * L.cap * (W->inter / 32));
   L.slot_out = take((size_t)n * W->hidden * 4);
   L.total = off;
   return L;
