@@ -30,6 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+# MI355X published dense matrix-core peaks (TFLOP/s).  The grouped GEMMs
+# take MXFP8 activations as the A operand, so even with E2M1 weights every
+# block-scaled MFMA issues at the 8-bit rate.
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}
 DOMINANT = "gate_up_decode_kernel"
 KERNEL_SOURCES = ["mixture_experts_decode_amd/csrc/decode.hip",
                   "mixture_experts_decode_amd/csrc/device.h"]
@@ -47,6 +51,10 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-copy-peak", action="store_true")
+    p.add_argument("--no-grouped", action="store_true",
+                   help="skip the expert-centric (grouped MFMA) report")
+    p.add_argument("--crossover", action="store_true",
+                   help="also sweep the MXFP4 layer over B with both paths")
     return p.parse_args()
 
 
@@ -236,6 +244,20 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, B, arrays)
+    del layers, arrays, w0
+    torch.cuda.empty_cache()
+
+    grouped = []
+    if not args.no_grouped:
+        # DeepSeek-V3-shaped layer at B = 256 (HBM-bound) and the Zipf
+        # prefill step (MFMA-bound)
+        for cid, t, bs, kind in ((3, 256, 64, None), (4, 16384, 128, "zipf")):
+            grouped.append(grouped_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t, bs, kind))
+            torch.cuda.empty_cache()
+
+    crossover = []
+    if args.crossover:
+        crossover = crossover_sweep(moe, W, torch, dev, stream, W.CONFIGS[5])
 
     value = main_res["TBps"]
     out = {
@@ -264,38 +286,169 @@ def main():
         "sweep": sweep,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "grouped": grouped,
     }
+    if crossover:
+        out["crossover"] = crossover
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, B, arrays):
-    """The float64 oracle timed on this host's cores on one full layer call of
-    the same workload (B tokens, its first routing draw)."""
+def _device_inputs(torch, dev, W, cfg, t, kind, variant=0):
+    x = W.activations(cfg, t, variant)
+    ids, wts = W.routing(cfg, t, kind=kind, variant=variant)
+    xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
+          else torch.from_numpy(x)).to(dev)
+    return xd, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), ids
+
+
+def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmup=3):
+    """Expert-centric path on one layer: the five calls moe_layer makes
+    (align-sort, gather + MXFP8 quantisation, gate_up GEMM, down GEMM,
+    combine), each bracketed by HIP events on the launch stream.  MFMA
+    utilisation counts useful FLOPs only (padding rows excluded)."""
+    arrays = W.all_experts(cfg)
+    Wd = moe.Weights.from_arrays(cfg, arrays)
+    del arrays
+    x, ids, wts, ids_np = _device_inputs(torch, dev, W, cfg, t, kind)
+    k, S = cfg.top_k, cfg.num_shared
+    slots = k + S
+    y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+    slot_out = torch.empty((t * slots, cfg.hidden), dtype=torch.float32, device=dev)
+    cap = moe.align_sort_capacity(t, k, cfg.num_experts, S, bs)
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        srt = moe.align_sort(ids, cfg.num_experts, S, bs)
+        rec(1)
+        xq, xs = moe.gather_quant(x, slots, srt["sorted_token_ids"],
+                                  srt["num_tokens_post_padded"], cap)
+        rec(2)
+        hq, hs = moe.grouped_gate_up(Wd, xq, xs, srt["expert_ids"], srt["num_tokens_post_padded"],
+                                     cap, bs)
+        rec(3)
+        moe.grouped_down(Wd, hq, hs, srt["sorted_token_ids"], srt["expert_ids"],
+                         srt["num_tokens_post_padded"], cap, bs, wts, t, k, slot_out=slot_out)
+        rec(4)
+        moe.combine(slot_out, t, slots, y=y)
+        rec(5)
+
+    step()
+    y_ref, chosen = moe.layer(Wd, x, ids, wts, path="grouped", block=bs)
+    torch.cuda.synchronize()
+    if not torch.equal(y, y_ref):
+        raise RuntimeError("timed grouped sequence differs from moe_layer(grouped)")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    names = ["align_sort", "gather_quant", "gate_up_gemm", "down_gemm", "combine"]
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+           for j, n in enumerate(names)}
+    total = float(np.mean([e[0].elapsed_time(e[5]) for e in evs])) * 1e3
+    entries = t * slots
+    fl_gu = 2.0 * entries * cfg.hidden * 2 * cfg.inter
+    fl_dn = 2.0 * entries * cfg.inter * cfg.hidden
+    peak = MFMA_PEAK_TFLOPS["fp8"]
+    u = len(W.touched_experts(cfg, ids_np))
+    wbytes = u * W.expert_bytes(cfg)
+    act = 2 if cfg.act == "bf16" else 4
+    io = t * cfg.hidden * act + ids_np.nbytes * 2 + t * cfg.hidden * 4
+    res = {"workload": cfg.name, "tokens": t, "block": bs, "routing": kind or cfg.routing,
+           "touched_experts": u, "capacity": cap,
+           "us_per_layer": round(total, 2),
+           "kernels_us": {n: round(v, 2) for n, v in per.items()},
+           "useful_TFLOP": round((fl_gu + fl_dn) / 1e12, 4),
+           "gate_up_TFLOPs": round(fl_gu / (per["gate_up_gemm"] * 1e-6) / 1e12, 1),
+           "down_TFLOPs": round(fl_dn / (per["down_gemm"] * 1e-6) / 1e12, 1),
+           "layer_TFLOPs": round((fl_gu + fl_dn) / (total * 1e-6) / 1e12, 1),
+           "mfma_peak_TFLOPs": peak,
+           "mfma_frac_gate_up": round(fl_gu / (per["gate_up_gemm"] * 1e-6) / 1e12 / peak, 4),
+           "mfma_frac_down": round(fl_dn / (per["down_gemm"] * 1e-6) / 1e12 / peak, 4),
+           "mfma_frac_layer": round((fl_gu + fl_dn) / (total * 1e-6) / 1e12 / peak, 4),
+           "algorithmic_TBps": round((wbytes + io) / (total * 1e-6) / 1e12, 3)}
+    print(f"[bench] grouped {cfg.name} T={t} bs={bs}: {total:.1f} us "
+          f"(gate_up {per['gate_up_gemm']:.1f}, down {per['down_gemm']:.1f})",
+          file=sys.stderr, flush=True)
+    del Wd
+    return res
+
+
+def crossover_sweep(moe, W, torch, dev, stream, cfg, steps=20, warmup=3, bs=64):
+    """Whole-layer time of both paths over the batch list, uniform and Zipf
+    routing, on one layer's weights (several routing draws cycled)."""
+    arrays = W.all_experts(cfg)
+    Wd = moe.Weights.from_arrays(cfg, arrays)
+    del arrays
+    out = []
+    for kind in ("uniform", "zipf"):
+        for t in cfg.batches:
+            ins = [_device_inputs(torch, dev, W, cfg, t, kind, v) for v in range(4)]
+            row = {"routing": kind, "B": t, "auto": moe.choose_path(Wd, t, cfg.top_k),
+                   "touched_mean": float(np.mean([len(W.touched_experts(cfg, i[3])) for i in ins]))}
+            for path in ("decode", "grouped"):
+                if path == "decode" and t * (cfg.top_k + cfg.num_shared) > 2048:
+                    continue
+                need = moe.layer_workspace_bytes(Wd, t, cfg.top_k, path, bs)
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+                y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+                for i in range(warmup):
+                    xd, idd, wd, _ = ins[i % 4]
+                    moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
+                torch.cuda.synchronize()
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                for i in range(steps):
+                    xd, idd, wd, _ = ins[i % 4]
+                    moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
+                s1.record(stream)
+                torch.cuda.synchronize()
+                row[path + "_us"] = round(s0.elapsed_time(s1) * 1e3 / steps, 2)
+            print(f"[bench] crossover {row}", file=sys.stderr, flush=True)
+            out.append(row)
+    del Wd
+    return out
+
+
+def cpu_baseline(cfg, B, arrays, budget_s=12.0, max_calls=8):
+    """The float64 oracle timed on this host's cores on whole layer calls of
+    the same workload (B tokens; successive routing draws) until about
+    `budget_s` seconds of CPU work have run (at most `max_calls` calls)."""
     import workloads as W
     from oracle import layer as L
-    x = W.activations(cfg, B, 0)
-    ids, wts = W.routing(cfg, B, variant=0)
 
     def get(e):
         return {k: (None if v is None else v[e]) for k, v in arrays.items()}
 
     kw = dict(fmt=cfg.fmt, num_experts=cfg.num_experts, num_shared=cfg.num_shared, get_expert=get)
-    t0 = time.perf_counter()
-    L.moe_layer(L.activations_f64(x, cfg.act), ids, wts, **kw)
-    dt = time.perf_counter() - t0
-    u = len(W.touched_experts(cfg, ids))
     act_bytes = 2 if cfg.act == "bf16" else 4
-    nbytes = u * W.expert_bytes(cfg) + B * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes \
-        + B * cfg.hidden * 4
+    spent, nbytes, calls, touched = 0.0, 0, 0, []
+    while calls < max_calls and (calls == 0 or spent < budget_s):
+        x = W.activations(cfg, B, calls)
+        ids, wts = W.routing(cfg, B, variant=calls)
+        t0 = time.perf_counter()
+        L.moe_layer(L.activations_f64(x, cfg.act), ids, wts, **kw)
+        spent += time.perf_counter() - t0
+        u = len(W.touched_experts(cfg, ids))
+        touched.append(u)
+        nbytes += u * W.expert_bytes(cfg) + B * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes \
+            + B * cfg.hidden * 4
+        calls += 1
+    dt = spent / calls
     try:
         import threadpoolctl
         threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count()
-    return {"value": round(nbytes / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
-            "kind": "oracle", "us_per_layer": round(dt * 1e6, 1),
+    return {"value": round(nbytes / spent / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "us_per_layer": round(dt * 1e6, 1), "seconds": round(spent, 2),
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"one full layer call of {cfg.name}, B={B} ({u} touched experts), float64"}
+            "sample": f"{calls} whole layer calls of {cfg.name} at B={B} (successive routing "
+                      f"draws, {min(touched)}-{max(touched)} touched experts), float64"}
 
 
 if __name__ == "__main__":

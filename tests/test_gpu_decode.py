@@ -171,8 +171,6 @@ def test_decode_full_size_sampled(lib, cid, t, kind):
     """Full configuration and batch, in the launch shape the benchmark times;
     the oracle checks a sample of tokens (tokens are independent)."""
     cfg = W.CONFIGS[cid]
-    if kind == "zipf":
-        cfg = cfg.replace(zipf_s=1.2)
     x, ids, w, h, y = _run_decode(lib, cfg, t, kind=kind)
     sample = sorted({0, t // 2, t - 1})
     x64 = L.activations_f64(x[sample], cfg.act)

@@ -78,7 +78,7 @@ CONFIGS = {
               "biased", batches=(1, 16, 64, 256)),
     4: Config(4, "prefill_zipf_mxfp8", 4096, 1536, 256, 8, 0, "mxfp8", "bf16", "zipf",
               zipf_s=1.1, batches=(16384,), blocks=(64, 128)),
-    5: Config(5, "mxfp4_sweep", 4096, 1536, 128, 8, 0, "mxfp4", "bf16", "uniform",
+    5: Config(5, "mxfp4_sweep", 4096, 1536, 128, 8, 0, "mxfp4", "bf16", "uniform", zipf_s=1.2,
               batches=(1, 2, 8, 32, 64, 128, 256)),
 }
 
