@@ -252,7 +252,8 @@ def main():
         # DeepSeek-V3-shaped layer at B = 256 (HBM-bound) and the Zipf
         # prefill step (MFMA-bound)
         for cid, t, bs, kind in ((3, 256, 64, None), (4, 16384, 128, "zipf")):
-            grouped.append(grouped_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t, bs, kind))
+            grouped.append(grouped_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t, bs, kind,
+                                          steps=min(args.steps, 20)))
             torch.cuda.empty_cache()
 
     crossover = []

@@ -242,7 +242,7 @@ moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const ui
   moe_status st = check_weights(W);
   if (st != MOE_OK) return st;
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
-  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
   if (capacity == 0) return MOE_OK;
   if (!xq || !xs || !expert_ids || !num_tokens_post_padded || !hq || !hs)
@@ -260,7 +260,7 @@ moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8
   if (st != MOE_OK) return st;
   if ((st = check_routing(W, T, k)) != MOE_OK) return st;
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
-  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
   if (capacity == 0 || T == 0) return MOE_OK;
   if (!hq || !hs || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !slot_out ||
@@ -283,7 +283,7 @@ int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
   if (check_weights(W) != MOE_OK || T < 0 || k < 0) return MOE_PATH_DECODE;
   const int64_t entries = (int64_t)T * (k + W->num_shared);
   if (!grouped_supported(W)) return MOE_PATH_DECODE;
-  if (W->hidden % 128 || W->inter % 64) return MOE_PATH_DECODE;
+  if (W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;
   if (entries > kDecodeMaxEntries) return MOE_PATH_GROUPED;
   return entries <= decode_entry_threshold(W) ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
 }
@@ -330,7 +330,7 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   }
   // grouped
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
-  if (W->hidden % 128 || W->inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
   const GroupedLayout L = grouped_layout(W, T, k, block_size);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARG;

@@ -177,6 +177,20 @@ hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* 
 
 // ---------------------------------------------------------------------------
 // grouped GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4
+//
+// A workgroup of 4 wavefronts computes a BM x BN tile: BM sorted rows (one
+// align-sort block, hence one expert) against BN weight rows.  Both operand
+// tiles travel HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4),
+// in NS stages of 128 K, so NS-1 stages are in flight while one is consumed
+// and no registers are spent on staging.  An LDS row holds the stage's 128
+// (FP4: 64) bytes with its 16-byte chunks XOR-swizzled by the row index: each
+// DMA instruction still writes 1 KB contiguously (8 or 16 whole rows), and the
+// MFMA operand reads of 8 / 16 consecutive rows land on distinct banks.  The
+// scales ride along, 4 bytes (four 32-K blocks) per row and stage, into a
+// slice private to each wavefront.  The grid is persistent: the tiles
+// (M-block, N-tile) are counted on the device from the padded total, split
+// evenly over the XCDs, and walked in groups of M-blocks so that concurrent
+// workgroups on one XCD share activation and weight rows in its L2.
 // ---------------------------------------------------------------------------
 
 namespace {
@@ -185,16 +199,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmBlock = 256;          // 4 wavefronts
-constexpr int kKStep = 64;               // K per MFMA
-constexpr int kARowPitch = 80;           // LDS bytes per staged A row (64 + pad)
+constexpr int kKStage = 128;             // K elements per pipeline stage
+constexpr int kLdsBytes = 160 * 1024;    // gfx950 LDS per workgroup
+constexpr int kGroupM = 4;               // M-blocks per raster group
 
 struct GemmArgs {
-  const uint8_t* a;        // activations [cap][K] E4M3 (the hi term for down)
+  const uint8_t* a;        // activations [cap][K] E4M3 (down: the hi term of h)
   const uint8_t* as;       // [cap][K/32] E8M0
   const uint8_t* a_lo;     // down: lo term of h [cap][K]
   const uint8_t* as_lo;    // down: [cap][K/32]
   const uint8_t* b;        // expert weights, rows of K (E4M3 or packed E2M1)
-  const void* bs;          // weight scales (E8M0 bytes or float tiles)
+  const void* bs;          // weight scales (E8M0 bytes or float 128x128 tiles)
   const int32_t* expert_ids;
   const int32_t* npp;
   const int32_t* sorted;   // down: entry of each sorted row
@@ -207,288 +222,421 @@ struct GemmArgs {
   int I, H;
   int b_row_bytes;
   int rows_per_expert;     // 2I (gate_up) or H (down)
-  int n_ntiles;            // workgroup tiles along N
+  int n_ntiles;            // tiles along N
   int k, slots, sentinel;
   int nxcd;
 };
 
-// Max over the 32 lanes of each half wave.
-__device__ __forceinline__ float half32_max(float x) {
-  x = fmaxf(x, dpp_f32<0x128>(x));
-  x = fmaxf(x, dpp_f32<0x124>(x));
-  x = fmaxf(x, dpp_f32<0x122>(x));
-  x = fmaxf(x, dpp_f32<0x121>(x));
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory-model fence of __syncthreads (which
+// would drain every DMA in flight).  This wavefront's LDS reads complete
+// before it arrives, so no buffer is overwritten under a pending read.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte chunk slot of chunk c in LDS row r: 8 chunks per row (8-bit rows of
+// 128 bytes) and 4 per row (E2M1 rows of 64 bytes).
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Max of x over lanes l and l ^ 32.
+__device__ __forceinline__ float pair32_max(float x) {
   const uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// B fragment of one K step for the weight row of this lane.  8-bit elements:
-// bytes [16h, 16h+16) and [32+16h, 32+16h+16) of the step (the gfx950 lane
-// layout of 8-bit MFMA operands); E2M1: 16 bytes holding K [32h, 32h+32).
-template <int BFMT>
-__device__ __forceinline__ i32x8 load_b_frag(const uint8_t* row, int step, int h) {
-  i32x8 v;
-  if constexpr (BFMT == W_MXFP4) {
-    const u32x4 q = load_stream16(row + step * (kKStep / 2) + 16 * h);
-    v = i32x8{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-  } else {
-    const u32x4 q0 = load_stream16(row + step * kKStep + 16 * h);
-    const u32x4 q1 = load_stream16(row + step * kKStep + 32 + 16 * h);
-    v = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
-              (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-  }
-  return v;
-}
+template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN>
+struct GemmShape {
+  static constexpr int TERMS = GATEUP ? 1 : 2;    // down reads h as hi + lo
+  static constexpr bool FP4 = BFMT == W_MXFP4;
+  static constexpr bool T128 = BFMT == W_FP8B128;
+  static constexpr int BRB = FP4 ? 64 : 128;       // weight bytes per row and stage
+  static constexpr int WROWS = BM / WM;            // wavefront sub-tile
+  static constexpr int WCOLS = BN / WN;
+  static constexpr int MF = WROWS / 32;
+  static constexpr int NF = WCOLS / 32;
+  static constexpr int A_BYTES = TERMS * BM * 128;
+  static constexpr int B_BYTES = BN * BRB;
+  static constexpr int SA = WROWS < 64 ? 64 : WROWS;              // scale dwords per term
+  static constexpr int SB = T128 ? 64 : (WCOLS < 64 ? 64 : WCOLS);
+  static constexpr int SLICE = (TERMS * SA + SB) * 4;             // per wavefront
+  static constexpr int STAGE = A_BYTES + B_BYTES + 4 * SLICE;
+  static constexpr int NS_FIT = kLdsBytes / STAGE;
+  static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
+  static constexpr int A_INSTR = A_BYTES / 4096;                  // per wavefront
+  static constexpr int B_INSTR = B_BYTES / 4096;
+  static constexpr int S_INSTR = TERMS * (SA / 64) + SB / 64;
+  static constexpr int L = A_INSTR + B_INSTR + S_INSTR;           // DMA ops per stage
+  static constexpr int ROWS_PER_BI = FP4 ? 16 : 8;                // rows per B instruction
+  static_assert(WM * WN == 4, "four wavefronts");
+  static_assert(WROWS % 32 == 0 && WCOLS % 32 == 0, "whole fragments");
+  static_assert(!GATEUP || NF % 2 == 0, "gate and up fragments pair up");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole DMA rounds");
+  static_assert(NS >= 2, "double buffering fits");
+  static_assert((NS - 2) * L < 64, "vmcnt range");
+};
 
-template <int BFMT, bool GATEUP, int MF, int NF>
+template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs g) {
-  constexpr int BS = MF * 32;
-  constexpr bool kTile128 = BFMT == W_FP8B128;   // float 128x128 weight scales
-  constexpr int TERMS = GATEUP ? 1 : 2;          // down reads h as hi + lo
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][TERMS][BS * kARowPitch];
+  using S = GemmShape<BFMT, GATEUP, BM, BN, WM, WN>;
+  constexpr int MF = S::MF, NF = S::NF, TERMS = S::TERMS, NS = S::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * S::STAGE];
+
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int r32 = lane & 31, h = lane >> 5;
+  const int wm = w / WN, wn = w % WN;
 
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x, g.nxcd);
-  const int mb = lb / g.n_ntiles;
-  const int nt = lb - mb * g.n_ntiles;
-  if (mb * BS >= *g.npp) return;
-  const int e = g.expert_ids[mb];
-  const int row0 = mb * BS;
-  const int nsteps = g.K / kKStep;
-
-  // this wavefront's NF fragments of 32 weight rows
-  int col[NF];           // output column (neuron or H index) of the lane's row
-  const uint8_t* brow[NF];
-  long long bidx[NF];    // global weight row index
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    int c, proj = 0;
-    if constexpr (GATEUP) {
-      const int nb = nt * (4 * (NF / 2) * 32) + w * ((NF / 2) * 32);
-      proj = f < NF / 2 ? 0 : 1;
-      c = nb + 32 * (f % (NF / 2)) + r32;
-    } else {
-      c = nt * (4 * NF * 32) + w * (NF * 32) + 32 * f + r32;
-    }
-    col[f] = c;
-    const int cc = min(c, g.N - 1);
-    bidx[f] = (long long)e * g.rows_per_expert + (long long)proj * g.I + cc;
-    brow[f] = g.b + bidx[f] * g.b_row_bytes;
-  }
+  const int nx = g.nxcd;
+  const int xcd = blockIdx.x % nx, local = blockIdx.x / nx, per_x = gridDim.x / nx;
+  const int n_mb = *g.npp / BM;
+  const int total = n_mb * g.n_ntiles;
+  const int chunk = (total + nx - 1) / nx;
+  const int t_end = min(total, (xcd + 1) * chunk);
+  const int nst = g.K / kKStage;
   const int k_blocks = g.K >> 5;
-  const int k_tiles = g.K >> 7;
 
-  f32x16 acc[MF][NF];
-#pragma unroll
-  for (int m = 0; m < MF; ++m)
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[m][f] = f32x16{0};
-  f32x16 part[kTile128 ? MF : 1][kTile128 ? NF : 1];
-  if constexpr (kTile128) {
-#pragma unroll
-    for (int m = 0; m < MF; ++m)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
-  }
-
-  // ---- staging of the activation tile(s) (BS rows x 64 bytes per step)
-  constexpr int kAChunks = BS * 4;                       // 16-byte chunks per step
-  constexpr int kAPerThread = (kAChunks + kGemmBlock - 1) / kGemmBlock;
-  u32x4 a_stage[TERMS][kAPerThread];
-  auto load_a = [&](int step) {
-#pragma unroll
-    for (int tm = 0; tm < TERMS; ++tm) {
-      const uint8_t* src = tm == 0 ? g.a : g.a_lo;
-#pragma unroll
-      for (int i = 0; i < kAPerThread; ++i) {
-        const int c = threadIdx.x + i * kGemmBlock;
-        if (c < kAChunks) {
-          const int r = c >> 2, sg = c & 3;
-          a_stage[tm][i] = load16(src + (size_t)(row0 + r) * g.K + step * kKStep + sg * 16);
-        }
-      }
+  // tile row of the weight operand -> weight row inside the expert
+  auto b_row = [&](int nt, int trow) -> int {
+    if constexpr (GATEUP) {
+      const int proj = trow >= BN / 2 ? 1 : 0;
+      const int n = min(nt * (BN / 2) + trow - proj * (BN / 2), g.N - 1);
+      return proj * g.I + n;
+    } else {
+      return min(nt * BN + trow, g.N - 1);
     }
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int tm = 0; tm < TERMS; ++tm) {
-#pragma unroll
-      for (int i = 0; i < kAPerThread; ++i) {
-        const int c = threadIdx.x + i * kGemmBlock;
-        if (c < kAChunks) {
-          const int r = c >> 2, sg = c & 3;
-          *reinterpret_cast<u32x4*>(&s_a[buf][tm][r * kARowPitch + sg * 16]) = a_stage[tm][i];
-        }
-      }
+  // tile row of weight row i (0 <= i < WCOLS) of this wavefront; fragment f
+  // covers i in [32f, 32f + 32)
+  auto wave_brow = [&](int i) -> int {
+    if constexpr (GATEUP) {
+      const int f = i >> 5, r = i & 31;
+      return f < NF / 2 ? wn * (S::WCOLS / 2) + 32 * f + r
+                        : BN / 2 + wn * (S::WCOLS / 2) + 32 * (f - NF / 2) + r;
+    } else {
+      return wn * S::WCOLS + i;
     }
   };
-  auto load_scales = [&](int step, int (&sa)[TERMS][MF], int (&sb)[NF]) {
+
+  // lane-constant LDS read offsets of the MFMA operands, per K step and half
+  int a8_off[2][2], b_off[2][2];
 #pragma unroll
-    for (int tm = 0; tm < TERMS; ++tm) {
-      const uint8_t* src = tm == 0 ? g.as : g.as_lo;
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int m = 0; m < MF; ++m)
-        sa[tm][m] = src[(size_t)(row0 + m * 32 + r32) * k_blocks + 2 * step + h];
+    for (int q = 0; q < 2; ++q) {
+      a8_off[st][q] = r32 * 128 + (((4 * st + 2 * q + h) ^ swz8(r32)) << 4);
+      b_off[st][q] = S::FP4 ? r32 * 64 + (((2 * st + h) ^ swz4(r32)) << 4) : a8_off[st][q];
     }
+
+  for (int t = xcd * chunk + local; t < t_end; t += per_x) {
+    const int gsz = kGroupM * g.n_ntiles;
+    const int grp = t / gsz;
+    const int rem = t - grp * gsz;
+    const int gm = min(kGroupM, n_mb - grp * kGroupM);
+    const int nt = rem / gm;
+    const int mb = grp * kGroupM + (rem - nt * gm);
+    const int e = g.expert_ids[mb];
+    const int row0 = mb * BM;
+
+    // ---- DMA sources: a uniform base per operand (advanced by the stage)
+    // plus a 32-bit per-lane offset that stays fixed for the whole tile
+    const uint8_t* a_base0 = g.a + (size_t)row0 * g.K;
+    const uint8_t* a_base1 = TERMS > 1 ? g.a_lo + (size_t)row0 * g.K : a_base0;
+    const uint8_t* b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
+    uint32_t a_off[S::A_INSTR];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if constexpr (kTile128) {
-        sb[f] = 127;
+    for (int i = 0; i < S::A_INSTR; ++i) {
+      const int j = (w + 4 * i) % (BM / 8);
+      const int row = 8 * j + (lane >> 3);
+      a_off[i] = (uint32_t)(row * g.K + (((lane & 7) ^ swz8(row)) << 4));
+    }
+    uint32_t b_off_g[S::B_INSTR];
+#pragma unroll
+    for (int i = 0; i < S::B_INSTR; ++i) {
+      const int j = w + 4 * i;
+      int row, c;
+      if constexpr (S::FP4) {
+        row = 16 * j + (lane >> 2);
+        c = (lane & 3) ^ swz4(row);
       } else {
-        sb[f] = reinterpret_cast<const uint8_t*>(g.bs)[bidx[f] * k_blocks + 2 * step + h];
+        row = 8 * j + (lane >> 3);
+        c = (lane & 7) ^ swz8(row);
       }
+      b_off_g[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (c << 4));
     }
-  };
-
-  i32x8 bcur[NF], bnxt[NF];
-  int sa_cur[TERMS][MF], sb_cur[NF], sa_nxt[TERMS][MF], sb_nxt[NF];
-  load_a(0);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) bcur[f] = load_b_frag<BFMT>(brow[f], 0, h);
-  load_scales(0, sa_cur, sb_cur);
-  store_a(0);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      load_a(s + 1);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) bnxt[f] = load_b_frag<BFMT>(brow[f], s + 1, h);
-      load_scales(s + 1, sa_nxt, sb_nxt);
-    }
-#pragma unroll
-    for (int m = 0; m < MF; ++m) {
-#pragma unroll
-      for (int tm = 0; tm < TERMS; ++tm) {
-        const uint8_t* ap = &s_a[buf][tm][(m * 32 + r32) * kARowPitch];
-        const u32x4 q0 = *reinterpret_cast<const u32x4*>(ap + 16 * h);
-        const u32x4 q1 = *reinterpret_cast<const u32x4*>(ap + 32 + 16 * h);
-        const i32x8 afrag = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
-                             (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if constexpr (kTile128) {
-            part[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                afrag, bcur[f], part[m][f], 0, 0, 0, sa_cur[tm][m], 0, sb_cur[f]);
-          } else {
-            acc[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                afrag, bcur[f], acc[m][f], 0, BFMT == W_MXFP4 ? 4 : 0, 0, sa_cur[tm][m], 0,
-                sb_cur[f]);
-          }
-        }
-      }
-    }
-    if constexpr (kTile128) {
-      if (s & 1) {   // a 128-wide K tile is complete: promote with its scale
-        const float* ts = reinterpret_cast<const float*>(g.bs);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const float sc = ts[(bidx[f] >> 7) * k_tiles + (s >> 1)];
-#pragma unroll
-          for (int m = 0; m < MF; ++m) {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], sc, acc[m][f][q]);
-            part[m][f] = f32x16{0};
-          }
-        }
-      }
-    }
-    if (more) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) bcur[f] = bnxt[f];
+    const uint8_t* sa_base0 = g.as + (size_t)row0 * k_blocks;
+    const uint8_t* sa_base1 = TERMS > 1 ? g.as_lo + (size_t)row0 * k_blocks : sa_base0;
+    const uint8_t* sb_base =
+        S::T128 ? reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * (g.rows_per_expert >> 7) * nst * 4
+                : reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * g.rows_per_expert * k_blocks;
+    uint32_t s_off[S::S_INSTR];
+    {
+      int q = 0;
 #pragma unroll
       for (int tm = 0; tm < TERMS; ++tm)
 #pragma unroll
-        for (int m = 0; m < MF; ++m) sa_cur[tm][m] = sa_nxt[tm][m];
+        for (int u = 0; u < S::SA / 64; ++u, ++q) {
+          const int rw = S::WROWS >= 64 ? 64 * u + lane : lane % S::WROWS;
+          s_off[q] = (uint32_t)((wm * S::WROWS + rw) * k_blocks);
+        }
 #pragma unroll
-      for (int f = 0; f < NF; ++f) sb_cur[f] = sb_nxt[f];
+      for (int u = 0; u < S::SB / 64; ++u, ++q) {
+        if constexpr (S::T128) {
+          s_off[q] = (uint32_t)((b_row(nt, wave_brow(32 * (lane % NF))) >> 7) * nst * 4);
+        } else {
+          const int i = S::WCOLS >= 64 ? 64 * u + lane : lane % S::WCOLS;
+          s_off[q] = (uint32_t)(b_row(nt, wave_brow(i)) * k_blocks);
+        }
+      }
     }
-    __syncthreads();
-  }
 
-  // ---- epilogue.  Accumulator element q of a 32x32 tile sits at row
-  // 8*(q/4) + 4*h + q%4 and column r32 of the tile.
-  if constexpr (GATEUP) {
+    auto issue = [&](int s, int buf) {
+      uint8_t* base = lds + buf * S::STAGE;
 #pragma unroll
-    for (int m = 0; m < MF; ++m) {
+      for (int i = 0; i < S::A_INSTR; ++i) {
+        const int j = w + 4 * i;               // WG instruction: plane j / (BM/8)
+        const uint8_t* src = (j >= BM / 8 ? a_base1 : a_base0) + s * 128;
+        dma16(src + a_off[i], base + (j / (BM / 8)) * BM * 128 + (j % (BM / 8)) * 1024);
+      }
 #pragma unroll
-      for (int f = 0; f < NF / 2; ++f) {
-        const int n = col[f];
+      for (int i = 0; i < S::B_INSTR; ++i)
+        dma16(b_base + s * S::BRB + b_off_g[i], base + S::A_BYTES + (w + 4 * i) * 1024);
+      uint8_t* slice = base + S::A_BYTES + S::B_BYTES + w * S::SLICE;
+      int q = 0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = row0 + m * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-          const float hv = swiglu(acc[m][f][q], acc[m][f + NF / 2][q]);
-          // hi = Q(h) per 32 neurons (the 32 lanes of this half wave), then
-          // lo = Q(h - hi): the residual is exact in FP32
-          const float amax = half32_max(n < g.N ? fabsf(hv) : 0.0f);
+      for (int tm = 0; tm < TERMS; ++tm)
+#pragma unroll
+        for (int u = 0; u < S::SA / 64; ++u, ++q)
+          dma4((tm ? sa_base1 : sa_base0) + s * 4 + s_off[q], slice + (tm * S::SA + 64 * u) * 4);
+#pragma unroll
+      for (int u = 0; u < S::SB / 64; ++u, ++q)
+        dma4(sb_base + s * 4 + s_off[q], slice + (TERMS * S::SA + 64 * u) * 4);
+    };
+
+    // acc[m][f]: 32 weight rows of fragment f (MFMA rows) x 32 sorted rows of
+    // fragment m (MFMA columns)
+    f32x16 acc[MF][NF];
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[m][f] = f32x16{0};
+
+    auto compute = [&](int buf) {
+      const uint8_t* base = lds + buf * S::STAGE;
+      const uint8_t* at = base + wm * S::WROWS * 128;
+      const uint8_t* bt = base + S::A_BYTES;
+      const uint32_t* slice =
+          reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES + w * S::SLICE);
+      uint32_t sa[TERMS][MF];
+#pragma unroll
+      for (int tm = 0; tm < TERMS; ++tm)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) sa[tm][m] = slice[tm * S::SA + 32 * m + r32];
+      uint32_t sb[NF];
+      float tsc[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if constexpr (S::T128) {
+          tsc[f] = __uint_as_float(slice[TERMS * S::SA + f]);
+          sb[f] = 0x7f7f7f7fu;
+        } else {
+          sb[f] = slice[TERMS * S::SA + 32 * f + r32];
+        }
+      }
+      f32x16 part[S::T128 ? MF : 1][S::T128 ? NF : 1];
+      if constexpr (S::T128) {
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int sh = 8 * (2 * st + h);
+        i32x8 bf[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint8_t* br = bt + wave_brow(32 * f) * S::BRB;
+          if constexpr (S::FP4) {
+            const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
+            bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], 0, 0, 0, 0};
+          } else {
+            const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
+            const u32x4 q1 = *reinterpret_cast<const u32x4*>(br + b_off[st][1]);
+            bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
+                          (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+          }
+        }
+#pragma unroll
+        for (int tm = 0; tm < TERMS; ++tm) {
+#pragma unroll
+          for (int m = 0; m < MF; ++m) {
+            const uint8_t* ar = at + tm * BM * 128 + m * 32 * 128;
+            const u32x4 q0 = *reinterpret_cast<const u32x4*>(ar + a8_off[st][0]);
+            const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a8_off[st][1]);
+            const i32x8 af = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
+                              (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+            const int sca = (int)((sa[tm][m] >> sh) & 0xffu);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const int scb = (int)((sb[f] >> sh) & 0xffu);
+              // weights as the first (row) operand, activations as the second
+              if constexpr (S::T128) {
+                part[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[f], af, part[m][f], 0, 0, 0, scb, 0, sca);
+              } else {
+                acc[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf[f], af, acc[m][f], S::FP4 ? 4 : 0, 0, 0, scb, 0, sca);
+              }
+            }
+          }
+        }
+      }
+      if constexpr (S::T128) {   // the stage is one 128-wide K tile: promote
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], tsc[f], acc[m][f][q]);
+      }
+    };
+
+    // ---- pipeline: NS-1 stages in flight
+    wait_vmem<0>();       // the previous tile's stores
+    wg_barrier();         // and every wavefront is done reading its buffers
+    const int pro = min(NS - 1, nst);
+    for (int s = 0; s < pro; ++s) issue(s, s);
+    int buf = 0;
+    for (int s = 0; s < nst; ++s) {
+      if (s + NS - 1 <= nst) wait_vmem<(NS - 2) * S::L>();
+      else wait_vmem<0>();
+      wg_barrier();
+      if (s + NS - 1 < nst) {
+        const int nb = buf == 0 ? NS - 1 : buf - 1;     // (s + NS - 1) % NS
+        issue(s + NS - 1, nb);
+      }
+      compute(buf);
+      buf = buf + 1 == NS ? 0 : buf + 1;
+    }
+
+    // ---- epilogue.  Register q of acc[m][f] holds weight row
+    // 8*(q/4) + 4*h + q%4 of fragment f for sorted row r32 of fragment m, so a
+    // lane owns 16 outputs of one row: four runs of 4 consecutive columns.
+    const int rbase = row0 + wm * S::WROWS;
+    if constexpr (GATEUP) {
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        const int row = rbase + m * 32 + r32;
+#pragma unroll
+        for (int f = 0; f < NF / 2; ++f) {
+          // 32 neurons = one MX block of h, split over this lane and lane ^ 32
+          const int n0 = nt * (BN / 2) + wn * (S::WCOLS / 2) + 32 * f;
+          float hv[16];
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            hv[q] = swiglu(acc[m][f][q], acc[m][f + NF / 2][q]);
+            amax = fmaxf(amax, fabsf(hv[q]));
+          }
+          amax = pair32_max(amax);
           const int e1 = mx_exponent(amax);
-          const uint32_t c1 = encode_e4m3(hv * pow2_neg(e1));
-          const float res = hv - decode_e4m3(c1) * pow2(e1);
-          const float rmax = half32_max(n < g.N ? fabsf(res) : 0.0f);
+          const float inv1 = pow2_neg(e1), sc1 = pow2(e1);
+          uint32_t c1[16];
+          float rmax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            c1[q] = encode_e4m3(hv[q] * inv1);
+            hv[q] -= decode_e4m3(c1[q]) * sc1;    // the residual is exact in FP32
+            rmax = fmaxf(rmax, fabsf(hv[q]));
+          }
+          rmax = pair32_max(rmax);
           const int e2 = mx_exponent(rmax);
-          const uint32_t c2 = encode_e4m3(res * pow2_neg(e2));
-          if (n < g.N) {
-            const size_t o = (size_t)row * g.I + n;
-            const size_t os = (size_t)row * (g.I >> 5) + (n >> 5);
-            g.hq[o] = (uint8_t)c1;
-            g.hq[(size_t)g.cap * g.I + o] = (uint8_t)c2;
-            if (r32 == 0) {
-              g.hs[os] = (uint8_t)(e1 + 127);
-              g.hs[(size_t)g.cap * (g.I >> 5) + os] = (uint8_t)(e2 + 127);
+          const float inv2 = pow2_neg(e2);
+          uint8_t* q_hi = g.hq + (size_t)row * g.I + n0 + 4 * h;
+          uint8_t* q_lo = q_hi + (size_t)g.cap * g.I;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            uint32_t whi = 0, wlo = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              whi |= c1[4 * r + b] << (8 * b);
+              wlo |= encode_e4m3(hv[4 * r + b] * inv2) << (8 * b);
+            }
+            *reinterpret_cast<uint32_t*>(q_hi + 8 * r) = whi;
+            *reinterpret_cast<uint32_t*>(q_lo + 8 * r) = wlo;
+          }
+          if (h == 0) {
+            const size_t os = (size_t)row * (g.I >> 5) + (n0 >> 5);
+            g.hs[os] = (uint8_t)(e1 + 127);
+            g.hs[(size_t)g.cap * (g.I >> 5) + os] = (uint8_t)(e2 + 127);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        const int row = rbase + m * 32 + r32;
+        const int ent = g.sorted[row];
+        if (ent < 0 || ent >= g.sentinel) continue;
+        const int tk = ent / g.slots, j = ent - tk * g.slots;
+        const float wgt = j < g.k ? g.wts[tk * g.k + j] : 1.0f;
+        float* out = g.out + (size_t)ent * g.H;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int c0 = nt * BN + wn * S::WCOLS + 32 * f + 4 * h;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (c0 + 8 * r < g.N) {
+              float4 v;
+              v.x = __fmul_rn(acc[m][f][4 * r + 0], wgt);
+              v.y = __fmul_rn(acc[m][f][4 * r + 1], wgt);
+              v.z = __fmul_rn(acc[m][f][4 * r + 2], wgt);
+              v.w = __fmul_rn(acc[m][f][4 * r + 3], wgt);
+              *reinterpret_cast<float4*>(out + c0 + 8 * r) = v;
             }
           }
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int m = 0; m < MF; ++m) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = row0 + m * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-        const int ent = g.sorted[row];
-        if (ent < 0 || ent >= g.sentinel) continue;
-        const int t = ent / g.slots, j = ent - t * g.slots;
-        const float wgt = j < g.k ? g.wts[t * g.k + j] : 1.0f;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if (col[f] < g.N) g.out[(size_t)ent * g.H + col[f]] = __fmul_rn(acc[m][f][q], wgt);
-        }
-      }
-    }
   }
 }
 
+// Tile shapes: BM is the align-sort block; BN weight rows per workgroup.
 template <int BFMT, bool GATEUP>
-hipError_t gemm_dispatch(const GemmArgs& a, int bs, int capacity, hipStream_t s) {
-  const int n_mblocks = capacity / bs;
-  if (n_mblocks == 0) return hipSuccess;
-  const dim3 grid(n_mblocks * a.n_ntiles), block(kGemmBlock);
-#define MOE_GG(MF, NF) hipLaunchKernelGGL((grouped_gemm_kernel<BFMT, GATEUP, MF, NF>), grid, block, 0, s, a)
-  if constexpr (BFMT == W_FP8B128) {
-    if (bs == 32) MOE_GG(1, 4);
-    else if (bs == 64) MOE_GG(2, 2);
-    else if (!GATEUP) MOE_GG(4, 1);
-    else return hipErrorNotSupported;
-  } else {
-    if (bs == 32) MOE_GG(1, 8);
-    else if (bs == 64) MOE_GG(2, 4);
-    else MOE_GG(4, 2);
-  }
+hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
+  GemmArgs a = a0;
+  const int nx = a.nxcd;
+  const int grid = std::max(nx, device_num_cus() / nx * nx);   // one workgroup per CU
+#define MOE_GG(BM, BN, WM, WN)                                                             \
+  do {                                                                                     \
+    a.n_ntiles = (GATEUP ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);           \
+    hipLaunchKernelGGL((grouped_gemm_kernel<BFMT, GATEUP, BM, BN, WM, WN>), dim3(grid),    \
+                       dim3(kGemmBlock), 0, s, a);                                         \
+  } while (0)
+  if (bs == 32) MOE_GG(32, 256, 1, 4);
+  else if (bs == 64) MOE_GG(64, 256, 1, 4);
+  else MOE_GG(128, 256, 2, 2);
 #undef MOE_GG
   return hipGetLastError();
-}
-
-// fragments per wavefront for a block size (as dispatched above)
-int gemm_nf(int fmt, int bs) {
-  if (fmt == W_FP8B128) return bs == 32 ? 4 : bs == 64 ? 2 : 1;
-  return bs == 32 ? 8 : bs == 64 ? 4 : 2;
 }
 
 }  // namespace
@@ -496,6 +644,7 @@ int gemm_nf(int fmt, int bs) {
 hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const uint8_t* xs,
                                   const int32_t* expert_ids, const int32_t* npp, int capacity,
                                   int bs, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+  if (capacity / bs == 0) return hipSuccess;
   GemmArgs a{};
   a.a = xq;
   a.as = xs;
@@ -512,15 +661,11 @@ hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const
   a.H = W.hidden;
   a.b_row_bytes = W.format == W_MXFP4 ? W.hidden / 2 : W.hidden;
   a.rows_per_expert = 2 * W.inter;
-  const int nf = gemm_nf(W.format, bs);
-  const int per_wg = 4 * (nf / 2) * 32;                   // neurons per workgroup
-  if (nf < 2) return hipErrorNotSupported;
-  a.n_ntiles = (W.inter + per_wg - 1) / per_wg;
   a.nxcd = device_num_xcds();
   switch (W.format) {
-    case W_MXFP8: return gemm_dispatch<W_MXFP8, true>(a, bs, capacity, s);
-    case W_MXFP4: return gemm_dispatch<W_MXFP4, true>(a, bs, capacity, s);
-    case W_FP8B128: return gemm_dispatch<W_FP8B128, true>(a, bs, capacity, s);
+    case W_MXFP8: return gemm_dispatch<W_MXFP8, true>(a, bs, s);
+    case W_MXFP4: return gemm_dispatch<W_MXFP4, true>(a, bs, s);
+    case W_FP8B128: return gemm_dispatch<W_FP8B128, true>(a, bs, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -529,6 +674,7 @@ hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const ui
                                const int32_t* sorted, const int32_t* expert_ids,
                                const int32_t* npp, int capacity, int bs, const float* wts, int T,
                                int k, float* slot_out, hipStream_t s) {
+  if (capacity / bs == 0) return hipSuccess;
   GemmArgs a{};
   a.a = hq;
   a.as = hs;
@@ -548,17 +694,14 @@ hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const ui
   a.H = W.hidden;
   a.b_row_bytes = W.format == W_MXFP4 ? W.inter / 2 : W.inter;
   a.rows_per_expert = W.hidden;
-  const int nf = gemm_nf(W.format, bs);
-  const int per_wg = 4 * nf * 32;
-  a.n_ntiles = (W.hidden + per_wg - 1) / per_wg;
   a.k = k;
   a.slots = k + W.num_shared;
   a.sentinel = T * a.slots;
   a.nxcd = device_num_xcds();
   switch (W.format) {
-    case W_MXFP8: return gemm_dispatch<W_MXFP8, false>(a, bs, capacity, s);
-    case W_MXFP4: return gemm_dispatch<W_MXFP4, false>(a, bs, capacity, s);
-    case W_FP8B128: return gemm_dispatch<W_FP8B128, false>(a, bs, capacity, s);
+    case W_MXFP8: return gemm_dispatch<W_MXFP8, false>(a, bs, s);
+    case W_MXFP4: return gemm_dispatch<W_MXFP4, false>(a, bs, s);
+    case W_FP8B128: return gemm_dispatch<W_FP8B128, false>(a, bs, s);
     default: return hipErrorNotSupported;
   }
 }
