@@ -10,20 +10,22 @@ namespace {
 
 constexpr int kGqBlock = 256;
 
-// E4M3FN code of a float already divided by its block scale: saturate to
-// +-448, round to nearest, ties to even; the sign bit follows the input.
-__device__ __forceinline__ uint32_t encode_e4m3(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    uint32_t u = __float_as_uint(a);
-    u += 0x7ffffu + ((u >> 20) & 1u);        // keep 3 mantissa bits, ties to even
-    code = (u >> 20) - ((127u - 7u) << 3);   // rebias the exponent 127 -> 7
-  }
-  return sign | code;
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Four floats, already divided by their block scale, -> four E4M3FN codes in
+// one dword (byte i = element i).  They are saturated to +-448 first (the
+// conversion itself gives NaN past the top of the format); the gfx950
+// conversion then rounds to nearest, ties to even, and keeps the sign of
+// values that round to zero.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                                                __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f), 1.0f, true);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
 }
 
 // Shared MX exponent of a block with maximum magnitude amax:
@@ -49,14 +51,6 @@ __device__ __forceinline__ float pow2_neg(int e) {
 }
 
 __device__ __forceinline__ float pow2(int e) { return pow2_neg(-e); }
-
-// E4M3FN code -> float (finite codes): e == 0 subnormal m * 2^-9.
-__device__ __forceinline__ float decode_e4m3(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 24;
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return __uint_as_float(__float_as_uint(mag) | sign);
-}
 
 // One wavefront per sorted row; each lane quantises whole 32-element blocks.
 template <bool XF32>
@@ -105,13 +99,9 @@ __global__ __launch_bounds__(kGqBlock) void gather_quant_kernel(
     const float inv = pow2_neg(e);
     u32x4 out[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c0 = encode_e4m3(v[4 * i + 0] * inv);
-      const uint32_t c1 = encode_e4m3(v[4 * i + 1] * inv);
-      const uint32_t c2 = encode_e4m3(v[4 * i + 2] * inv);
-      const uint32_t c3 = encode_e4m3(v[4 * i + 3] * inv);
-      out[i >> 2][i & 3] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
+    for (int i = 0; i < 8; ++i)
+      out[i >> 2][i & 3] = e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv,
+                                  v[4 * i + 3] * inv);
     uint8_t* dq = xq + (size_t)r * H + b * 32;
     *reinterpret_cast<u32x4*>(dq) = out[0];
     *reinterpret_cast<u32x4*>(dq + 16) = out[1];
@@ -181,16 +171,19 @@ hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* 
 // A workgroup of 4 wavefronts computes a BM x BN tile: BM sorted rows (one
 // align-sort block, hence one expert) against BN weight rows.  Both operand
 // tiles travel HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4),
-// in NS stages of 128 K, so NS-1 stages are in flight while one is consumed
-// and no registers are spent on staging.  An LDS row holds the stage's 128
-// (FP4: 64) bytes with its 16-byte chunks XOR-swizzled by the row index: each
-// DMA instruction still writes 1 KB contiguously (8 or 16 whole rows), and the
-// MFMA operand reads of 8 / 16 consecutive rows land on distinct banks.  The
-// scales ride along, 4 bytes (four 32-K blocks) per row and stage, into a
-// slice private to each wavefront.  The grid is persistent: the tiles
-// (M-block, N-tile) are counted on the device from the padded total, split
-// evenly over the XCDs, and walked in groups of M-blocks so that concurrent
-// workgroups on one XCD share activation and weight rows in its L2.
+// in NS stages of 64 * KSTEPS K, so NS-1 stages are in flight while one is
+// consumed and no registers are spent on staging.  An LDS row holds one
+// stage of a matrix row with its 16-byte chunks XOR-swizzled by the row
+// index: every DMA instruction still writes 1 KB contiguously (whole rows),
+// and the MFMA operand reads of 8 or 16 consecutive rows land on distinct
+// banks.  The MX scales ride along (one dword = four 32-K blocks per row).
+// Weights are the MFMA row operand and activations the column operand, so a
+// lane ends up with 16 outputs of one sorted row.  The grid is persistent:
+// the tiles (M-block, N-tile) are counted on the device from the padded
+// total, split evenly over the XCDs and walked in groups of M-blocks, so that
+// concurrent workgroups on one XCD share activation and weight rows in L2.
+// The L2 -> CU path (about 12.5 TB/s over the chip in whole 128-byte lines,
+// measured) rather than the matrix cores bounds the large-batch tiles.
 // ---------------------------------------------------------------------------
 
 namespace {
@@ -199,7 +192,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmBlock = 256;          // 4 wavefronts
-constexpr int kKStage = 128;             // K elements per pipeline stage
 constexpr int kLdsBytes = 160 * 1024;    // gfx950 LDS per workgroup
 constexpr int kGroupM = 4;               // M-blocks per raster group
 
@@ -251,10 +243,15 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16-byte chunk slot of chunk c in LDS row r: 8 chunks per row (8-bit rows of
-// 128 bytes) and 4 per row (E2M1 rows of 64 bytes).
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// LDS slot of 16-byte chunk c of row r is c ^ swz<P>(r) for rows of P chunks
+// (P = 8, 4, 2: rows of 128, 64, 32 bytes): a bijection per row that spreads
+// 8 (and 16) consecutive rows reading the same chunk over distinct banks.
+template <int P>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (P == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else if constexpr (P == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return ((r >> 2) ^ (r >> 3)) & 1;
+}
 
 // Max of x over lanes l and l ^ 32.
 __device__ __forceinline__ float pair32_max(float x) {
@@ -263,29 +260,38 @@ __device__ __forceinline__ float pair32_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN>
+template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN, int KSTEPS>
 struct GemmShape {
   static constexpr int TERMS = GATEUP ? 1 : 2;    // down reads h as hi + lo
   static constexpr bool FP4 = BFMT == W_MXFP4;
   static constexpr bool T128 = BFMT == W_FP8B128;
-  static constexpr int BRB = FP4 ? 64 : 128;       // weight bytes per row and stage
+  static constexpr int KSTAGE = 64 * KSTEPS;       // K elements per stage
+  static constexpr int ARB = KSTAGE;               // activation bytes per row and stage
+  static constexpr int BRB = FP4 ? KSTAGE / 2 : KSTAGE;
+  static constexpr int AP = ARB / 16, BP = BRB / 16;   // 16-byte chunks per LDS row
   static constexpr int WROWS = BM / WM;            // wavefront sub-tile
   static constexpr int WCOLS = BN / WN;
   static constexpr int MF = WROWS / 32;
   static constexpr int NF = WCOLS / 32;
-  static constexpr int A_BYTES = TERMS * BM * 128;
+  static constexpr int A_BYTES = TERMS * BM * ARB;
   static constexpr int B_BYTES = BN * BRB;
-  static constexpr int SA = WROWS < 64 ? 64 : WROWS;              // scale dwords per term
-  static constexpr int SB = T128 ? 64 : (WCOLS < 64 ? 64 : WCOLS);
-  static constexpr int SLICE = (TERMS * SA + SB) * 4;             // per wavefront
-  static constexpr int STAGE = A_BYTES + B_BYTES + 4 * SLICE;
+  // activation scales: shared by the workgroup when every wavefront covers
+  // all BM = 128 rows (wavefront w loads rows 32w..32w+31 into a 64-dword
+  // slot, upper half duplicated), else one slice per wavefront of its rows
+  static constexpr bool AS_COOP = WM == 1 && BM == 128;
+  static constexpr int SA = WROWS < 64 ? 64 : WROWS;
+  static constexpr int AS_BYTES = AS_COOP ? TERMS * 4 * 64 * 4 : 4 * TERMS * SA * 4;
+  static constexpr int SB = T128 ? 64 : (WCOLS < 64 ? 64 : WCOLS);   // per wavefront
+  static constexpr int BS_BYTES = 4 * SB * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   static constexpr int NS_FIT = kLdsBytes / STAGE;
   static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
-  static constexpr int A_INSTR = A_BYTES / 4096;                  // per wavefront
+  static constexpr int A_INSTR = A_BYTES / 4096;   // per wavefront
   static constexpr int B_INSTR = B_BYTES / 4096;
-  static constexpr int S_INSTR = TERMS * (SA / 64) + SB / 64;
-  static constexpr int L = A_INSTR + B_INSTR + S_INSTR;           // DMA ops per stage
-  static constexpr int ROWS_PER_BI = FP4 ? 16 : 8;                // rows per B instruction
+  static constexpr int SA_INSTR = AS_COOP ? TERMS : TERMS * (SA / 64);
+  static constexpr int SB_INSTR = SB / 64;
+  static constexpr int L = A_INSTR + B_INSTR + SA_INSTR + SB_INSTR;   // DMA ops per stage
+  static_assert(KSTEPS == 1 || KSTEPS == 2, "stage depth");
   static_assert(WM * WN == 4, "four wavefronts");
   static_assert(WROWS % 32 == 0 && WCOLS % 32 == 0, "whole fragments");
   static_assert(!GATEUP || NF % 2 == 0, "gate and up fragments pair up");
@@ -294,9 +300,9 @@ struct GemmShape {
   static_assert((NS - 2) * L < 64, "vmcnt range");
 };
 
-template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN>
+template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN, int KSTEPS>
 __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs g) {
-  using S = GemmShape<BFMT, GATEUP, BM, BN, WM, WN>;
+  using S = GemmShape<BFMT, GATEUP, BM, BN, WM, WN, KSTEPS>;
   constexpr int MF = S::MF, NF = S::NF, TERMS = S::TERMS, NS = S::NS;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * S::STAGE];
 
@@ -311,8 +317,9 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
   const int total = n_mb * g.n_ntiles;
   const int chunk = (total + nx - 1) / nx;
   const int t_end = min(total, (xcd + 1) * chunk);
-  const int nst = g.K / kKStage;
+  const int nst = g.K / S::KSTAGE;
   const int k_blocks = g.K >> 5;
+  const int k_tiles = g.K >> 7;
 
   // tile row of the weight operand -> weight row inside the expert
   auto b_row = [&](int nt, int trow) -> int {
@@ -336,14 +343,17 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     }
   };
 
-  // lane-constant LDS read offsets of the MFMA operands, per K step and half
-  int a8_off[2][2], b_off[2][2];
+  // lane-constant LDS read offsets of the MFMA operands, per K step and half:
+  // an 8-bit operand lane holds bytes [16h, 16h+16) and [32+16h, 32+16h+16)
+  // of the 64-K step, an E2M1 lane bytes [16h, 16h+16) of its 32-byte step
+  int a_off[KSTEPS][2], b_off[KSTEPS][2];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      a8_off[st][q] = r32 * 128 + (((4 * st + 2 * q + h) ^ swz8(r32)) << 4);
-      b_off[st][q] = S::FP4 ? r32 * 64 + (((2 * st + h) ^ swz4(r32)) << 4) : a8_off[st][q];
+      a_off[st][q] = r32 * S::ARB + (((4 * st + 2 * q + h) ^ swz<S::AP>(r32)) << 4);
+      b_off[st][q] = S::FP4 ? r32 * S::BRB + (((2 * st + h) ^ swz<S::BP>(r32)) << 4)
+                            : r32 * S::BRB + (((4 * st + 2 * q + h) ^ swz<S::BP>(r32)) << 4);
     }
 
   for (int t = xcd * chunk + local; t < t_end; t += per_x) {
@@ -355,80 +365,84 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     const int mb = grp * kGroupM + (rem - nt * gm);
     const int e = g.expert_ids[mb];
     const int row0 = mb * BM;
+    // the per-lane DMA offsets are recomputed for every tile (a few VALU
+    // operations) rather than hoisted out of the tile loop and spilled
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 
     // ---- DMA sources: a uniform base per operand (advanced by the stage)
     // plus a 32-bit per-lane offset that stays fixed for the whole tile
     const uint8_t* a_base0 = g.a + (size_t)row0 * g.K;
     const uint8_t* a_base1 = TERMS > 1 ? g.a_lo + (size_t)row0 * g.K : a_base0;
     const uint8_t* b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
-    uint32_t a_off[S::A_INSTR];
+    constexpr int AR_I = 1024 / S::ARB, BR_I = 1024 / S::BRB;   // rows per DMA instruction
+    uint32_t a_src[S::A_INSTR];
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
-      const int j = (w + 4 * i) % (BM / 8);
-      const int row = 8 * j + (lane >> 3);
-      a_off[i] = (uint32_t)(row * g.K + (((lane & 7) ^ swz8(row)) << 4));
+      const int j = (w + 4 * i) % (BM / AR_I);
+      const int row = AR_I * j + ln / S::AP;
+      a_src[i] = (uint32_t)(row * g.K + (((ln % S::AP) ^ swz<S::AP>(row)) << 4));
     }
-    uint32_t b_off_g[S::B_INSTR];
+    uint32_t b_src[S::B_INSTR];
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i) {
-      const int j = w + 4 * i;
-      int row, c;
-      if constexpr (S::FP4) {
-        row = 16 * j + (lane >> 2);
-        c = (lane & 3) ^ swz4(row);
-      } else {
-        row = 8 * j + (lane >> 3);
-        c = (lane & 7) ^ swz8(row);
-      }
-      b_off_g[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (c << 4));
+      const int row = BR_I * (w + 4 * i) + ln / S::BP;
+      b_src[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (((ln % S::BP) ^ swz<S::BP>(row)) << 4));
     }
     const uint8_t* sa_base0 = g.as + (size_t)row0 * k_blocks;
     const uint8_t* sa_base1 = TERMS > 1 ? g.as_lo + (size_t)row0 * k_blocks : sa_base0;
     const uint8_t* sb_base =
-        S::T128 ? reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * (g.rows_per_expert >> 7) * nst * 4
+        S::T128 ? reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * (g.rows_per_expert >> 7) * k_tiles * 4
                 : reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * g.rows_per_expert * k_blocks;
-    uint32_t s_off[S::S_INSTR];
-    {
-      int q = 0;
+    uint32_t sa_src[S::SA_INSTR];
+    int sa_dst[S::SA_INSTR];
 #pragma unroll
-      for (int tm = 0; tm < TERMS; ++tm)
+    for (int q = 0; q < S::SA_INSTR; ++q) {
+      if constexpr (S::AS_COOP) {
+        sa_src[q] = (uint32_t)((32 * w + (ln & 31)) * k_blocks);
+        sa_dst[q] = (q * 256 + w * 64) * 4;                // term q, slot w
+      } else {
+        const int tm = q / (S::SA / 64), u = q % (S::SA / 64);
+        const int rw = S::WROWS >= 64 ? 64 * u + ln : ln % S::WROWS;
+        sa_src[q] = (uint32_t)((wm * S::WROWS + rw) * k_blocks);
+        sa_dst[q] = ((w * TERMS + tm) * S::SA + 64 * u) * 4;
+      }
+    }
+    uint32_t sb_src[S::SB_INSTR];
 #pragma unroll
-        for (int u = 0; u < S::SA / 64; ++u, ++q) {
-          const int rw = S::WROWS >= 64 ? 64 * u + lane : lane % S::WROWS;
-          s_off[q] = (uint32_t)((wm * S::WROWS + rw) * k_blocks);
-        }
-#pragma unroll
-      for (int u = 0; u < S::SB / 64; ++u, ++q) {
-        if constexpr (S::T128) {
-          s_off[q] = (uint32_t)((b_row(nt, wave_brow(32 * (lane % NF))) >> 7) * nst * 4);
-        } else {
-          const int i = S::WCOLS >= 64 ? 64 * u + lane : lane % S::WCOLS;
-          s_off[q] = (uint32_t)(b_row(nt, wave_brow(i)) * k_blocks);
-        }
+    for (int u = 0; u < S::SB_INSTR; ++u) {
+      if constexpr (S::T128) {
+        sb_src[u] = (uint32_t)((b_row(nt, wave_brow(32 * (ln % NF))) >> 7) * k_tiles * 4);
+      } else {
+        const int i = S::WCOLS >= 64 ? 64 * u + ln : ln % S::WCOLS;
+        sb_src[u] = (uint32_t)(b_row(nt, wave_brow(i)) * k_blocks);
       }
     }
 
+    // stage s reads the scale dword holding K blocks [4 * (s*KSTEPS/2), +4)
     auto issue = [&](int s, int buf) {
       uint8_t* base = lds + buf * S::STAGE;
+      const int ks = s * S::KSTAGE;                   // first K element of the stage
 #pragma unroll
       for (int i = 0; i < S::A_INSTR; ++i) {
-        const int j = w + 4 * i;               // WG instruction: plane j / (BM/8)
-        const uint8_t* src = (j >= BM / 8 ? a_base1 : a_base0) + s * 128;
-        dma16(src + a_off[i], base + (j / (BM / 8)) * BM * 128 + (j % (BM / 8)) * 1024);
+        const int j = w + 4 * i;                      // WG instruction: plane j / (BM / AR_I)
+        const uint8_t* src = (j >= BM / AR_I ? a_base1 : a_base0) + ks;
+        dma16(src + a_src[i], base + (j / (BM / AR_I)) * BM * S::ARB + (j % (BM / AR_I)) * 1024);
       }
 #pragma unroll
       for (int i = 0; i < S::B_INSTR; ++i)
-        dma16(b_base + s * S::BRB + b_off_g[i], base + S::A_BYTES + (w + 4 * i) * 1024);
-      uint8_t* slice = base + S::A_BYTES + S::B_BYTES + w * S::SLICE;
-      int q = 0;
+        dma16(b_base + (S::FP4 ? ks / 2 : ks) + b_src[i], base + S::A_BYTES + (w + 4 * i) * 1024);
+      const int sdw = (ks >> 7) * 4;                  // byte offset of the scale dword
+      uint8_t* as_lds = base + S::A_BYTES + S::B_BYTES;
 #pragma unroll
-      for (int tm = 0; tm < TERMS; ++tm)
+      for (int q = 0; q < S::SA_INSTR; ++q) {
+        const int tm = S::AS_COOP ? q : q / (S::SA / 64);
+        dma4((tm ? sa_base1 : sa_base0) + sdw + sa_src[q], as_lds + sa_dst[q]);
+      }
+      uint8_t* bs_lds = as_lds + S::AS_BYTES + w * S::SB * 4;
 #pragma unroll
-        for (int u = 0; u < S::SA / 64; ++u, ++q)
-          dma4((tm ? sa_base1 : sa_base0) + s * 4 + s_off[q], slice + (tm * S::SA + 64 * u) * 4);
-#pragma unroll
-      for (int u = 0; u < S::SB / 64; ++u, ++q)
-        dma4(sb_base + s * 4 + s_off[q], slice + (TERMS * S::SA + 64 * u) * 4);
+      for (int u = 0; u < S::SB_INSTR; ++u)
+        dma4(sb_base + (S::T128 ? (ks >> 7) * 4 : sdw) + sb_src[u], bs_lds + 64 * u * 4);
     };
 
     // acc[m][f]: 32 weight rows of fragment f (MFMA rows) x 32 sorted rows of
@@ -438,39 +452,44 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     for (int m = 0; m < MF; ++m)
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[m][f] = f32x16{0};
+    f32x16 part[S::T128 ? MF : 1][S::T128 ? NF : 1];
+    if constexpr (S::T128) {
+#pragma unroll
+      for (int m = 0; m < MF; ++m)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
+    }
 
-    auto compute = [&](int buf) {
+    auto compute = [&](int s, int buf) {
       const uint8_t* base = lds + buf * S::STAGE;
-      const uint8_t* at = base + wm * S::WROWS * 128;
+      const uint8_t* at = base + wm * S::WROWS * S::ARB;
       const uint8_t* bt = base + S::A_BYTES;
-      const uint32_t* slice =
-          reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES + w * S::SLICE);
+      const uint32_t* as_lds = reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES);
+      const uint32_t* bs_lds = as_lds + S::AS_BYTES / 4 + w * S::SB;
       uint32_t sa[TERMS][MF];
 #pragma unroll
       for (int tm = 0; tm < TERMS; ++tm)
 #pragma unroll
-        for (int m = 0; m < MF; ++m) sa[tm][m] = slice[tm * S::SA + 32 * m + r32];
+        for (int m = 0; m < MF; ++m) {
+          if constexpr (S::AS_COOP) sa[tm][m] = as_lds[tm * 256 + m * 64 + r32];
+          else sa[tm][m] = as_lds[(w * TERMS + tm) * S::SA + 32 * m + r32];
+        }
       uint32_t sb[NF];
       float tsc[NF];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if constexpr (S::T128) {
-          tsc[f] = __uint_as_float(slice[TERMS * S::SA + f]);
+          tsc[f] = __uint_as_float(bs_lds[f]);
           sb[f] = 0x7f7f7f7fu;
         } else {
-          sb[f] = slice[TERMS * S::SA + 32 * f + r32];
+          sb[f] = bs_lds[32 * f + r32];
         }
       }
-      f32x16 part[S::T128 ? MF : 1][S::T128 ? NF : 1];
-      if constexpr (S::T128) {
+      // byte of the scale dword for K step st of this stage, K block h
+      const int sbyte0 = KSTEPS == 2 ? 0 : 2 * (s & 1);
 #pragma unroll
-        for (int m = 0; m < MF; ++m)
-#pragma unroll
-          for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int sh = 8 * (2 * st + h);
+      for (int st = 0; st < KSTEPS; ++st) {
+        const int sh = 8 * (sbyte0 + 2 * st + h);
         i32x8 bf[NF];
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -489,9 +508,9 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
         for (int tm = 0; tm < TERMS; ++tm) {
 #pragma unroll
           for (int m = 0; m < MF; ++m) {
-            const uint8_t* ar = at + tm * BM * 128 + m * 32 * 128;
-            const u32x4 q0 = *reinterpret_cast<const u32x4*>(ar + a8_off[st][0]);
-            const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a8_off[st][1]);
+            const uint8_t* ar = at + tm * BM * S::ARB + m * 32 * S::ARB;
+            const u32x4 q0 = *reinterpret_cast<const u32x4*>(ar + a_off[st][0]);
+            const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a_off[st][1]);
             const i32x8 af = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
                               (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
             const int sca = (int)((sa[tm][m] >> sh) & 0xffu);
@@ -510,13 +529,18 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
           }
         }
       }
-      if constexpr (S::T128) {   // the stage is one 128-wide K tile: promote
+      if constexpr (S::T128) {
+        // a 128-wide K tile is complete: promote it with its float scale
+        if (KSTEPS == 2 || (s & 1)) {
 #pragma unroll
-        for (int m = 0; m < MF; ++m)
+          for (int m = 0; m < MF; ++m)
 #pragma unroll
-          for (int f = 0; f < NF; ++f)
+            for (int f = 0; f < NF; ++f) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], tsc[f], acc[m][f][q]);
+              for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], tsc[f], acc[m][f][q]);
+              part[m][f] = f32x16{0};
+            }
+        }
       }
     };
 
@@ -534,7 +558,7 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
         const int nb = buf == 0 ? NS - 1 : buf - 1;     // (s + NS - 1) % NS
         issue(s + NS - 1, nb);
       }
-      compute(buf);
+      compute(s, buf);
       buf = buf + 1 == NS ? 0 : buf + 1;
     }
 
@@ -560,13 +584,21 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
           amax = pair32_max(amax);
           const int e1 = mx_exponent(amax);
           const float inv1 = pow2_neg(e1), sc1 = pow2(e1);
-          uint32_t c1[16];
+          uint32_t whi[4];
           float rmax = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            c1[q] = encode_e4m3(hv[q] * inv1);
-            hv[q] -= decode_e4m3(c1[q]) * sc1;    // the residual is exact in FP32
-            rmax = fmaxf(rmax, fabsf(hv[q]));
+          for (int r = 0; r < 4; ++r) {
+            whi[r] = e4m3x4(hv[4 * r] * inv1, hv[4 * r + 1] * inv1, hv[4 * r + 2] * inv1,
+                            hv[4 * r + 3] * inv1);
+            // h - hi is exact in FP32
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(whi[r], 1.0f, false);
+            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(whi[r], 1.0f, true);
+            hv[4 * r + 0] -= d0.x * sc1;
+            hv[4 * r + 1] -= d0.y * sc1;
+            hv[4 * r + 2] -= d1.x * sc1;
+            hv[4 * r + 3] -= d1.y * sc1;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) rmax = fmaxf(rmax, fabsf(hv[4 * r + b]));
           }
           rmax = pair32_max(rmax);
           const int e2 = mx_exponent(rmax);
@@ -575,14 +607,9 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
           uint8_t* q_lo = q_hi + (size_t)g.cap * g.I;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            uint32_t whi = 0, wlo = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              whi |= c1[4 * r + b] << (8 * b);
-              wlo |= encode_e4m3(hv[4 * r + b] * inv2) << (8 * b);
-            }
-            *reinterpret_cast<uint32_t*>(q_hi + 8 * r) = whi;
-            *reinterpret_cast<uint32_t*>(q_lo + 8 * r) = wlo;
+            *reinterpret_cast<uint32_t*>(q_hi + 8 * r) = whi[r];
+            *reinterpret_cast<uint32_t*>(q_lo + 8 * r) =
+                e4m3x4(hv[4 * r] * inv2, hv[4 * r + 1] * inv2, hv[4 * r + 2] * inv2, hv[4 * r + 3] * inv2);
           }
           if (h == 0) {
             const size_t os = (size_t)row * (g.I >> 5) + (n0 >> 5);
@@ -621,20 +648,27 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
 }
 
 // Tile shapes: BM is the align-sort block; BN weight rows per workgroup.
+// Blocks of 32 / 64 rows stream their experts' weights (one M-block per
+// expert at decode-like batches, HBM-bound); 128-row blocks take a 128 x 512
+// tile in 64-K stages, the widest that three stages of LDS hold.
 template <int BFMT, bool GATEUP>
 hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
   GemmArgs a = a0;
   const int nx = a.nxcd;
   const int grid = std::max(nx, device_num_cus() / nx * nx);   // one workgroup per CU
-#define MOE_GG(BM, BN, WM, WN)                                                             \
-  do {                                                                                     \
-    a.n_ntiles = (GATEUP ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);           \
-    hipLaunchKernelGGL((grouped_gemm_kernel<BFMT, GATEUP, BM, BN, WM, WN>), dim3(grid),    \
-                       dim3(kGemmBlock), 0, s, a);                                         \
+#define MOE_GG(BM, BN, WM, WN, KS)                                                          \
+  do {                                                                                      \
+    a.n_ntiles = (GATEUP ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);            \
+    hipLaunchKernelGGL((grouped_gemm_kernel<BFMT, GATEUP, BM, BN, WM, WN, KS>), dim3(grid), \
+                       dim3(kGemmBlock), 0, s, a);                                          \
   } while (0)
-  if (bs == 32) MOE_GG(32, 256, 1, 4);
-  else if (bs == 64) MOE_GG(64, 256, 1, 4);
-  else MOE_GG(128, 256, 2, 2);
+  if (bs == 32) {
+    MOE_GG(32, 256, 1, 4, 2);
+  } else if (bs == 64) {
+    MOE_GG(64, 256, 1, 4, 2);
+  } else {
+    MOE_GG(128, 256, 2, 2, 2);
+  }
 #undef MOE_GG
   return hipGetLastError();
 }
