@@ -258,7 +258,11 @@ def main():
 
     crossover = []
     if args.crossover:
-        crossover = crossover_sweep(moe, W, torch, dev, stream, W.CONFIGS[5])
+        for cid, batches in ((5, None), (2, (1, 4, 8, 16, 32, 64, 128, 256)),
+                             (3, (1, 8, 16, 32, 64, 128, 224))):
+            crossover += crossover_sweep(moe, W, torch, dev, stream, W.CONFIGS[cid], batches=batches,
+                                         kinds=("uniform", "zipf") if cid == 5 else (None,))
+            torch.cuda.empty_cache()
 
     value = main_res["TBps"]
     out = {
@@ -378,17 +382,21 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
     return res
 
 
-def crossover_sweep(moe, W, torch, dev, stream, cfg, steps=20, warmup=3, bs=64):
-    """Whole-layer time of both paths over the batch list, uniform and Zipf
-    routing, on one layer's weights (several routing draws cycled)."""
+def crossover_sweep(moe, W, torch, dev, stream, cfg, batches=None, kinds=(None,), steps=20,
+                    warmup=3, bs=64):
+    """Whole-layer time of both paths over a batch list (the configuration's
+    own by default) and routing kinds (None: the configuration's own), on one
+    layer's weights with several routing draws cycled."""
     arrays = W.all_experts(cfg)
     Wd = moe.Weights.from_arrays(cfg, arrays)
     del arrays
     out = []
-    for kind in ("uniform", "zipf"):
-        for t in cfg.batches:
+    for kind in kinds:
+        for t in batches or cfg.batches:
             ins = [_device_inputs(torch, dev, W, cfg, t, kind, v) for v in range(4)]
-            row = {"routing": kind, "B": t, "auto": moe.choose_path(Wd, t, cfg.top_k),
+            row = {"workload": cfg.name, "routing": kind or cfg.routing, "B": t,
+                   "entries": t * (cfg.top_k + cfg.num_shared),
+                   "auto": moe.choose_path(Wd, t, cfg.top_k),
                    "touched_mean": float(np.mean([len(W.touched_experts(cfg, i[3])) for i in ins]))}
             for path in ("decode", "grouped"):
                 if path == "decode" and t * (cfg.top_k + cfg.num_shared) > 2048:

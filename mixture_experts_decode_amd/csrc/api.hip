@@ -4,6 +4,9 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include <cmath>
+#include <algorithm>
+
 #include "moe_mi355x.h"
 #include "moe_mi355x_util.h"
 
@@ -69,12 +72,41 @@ bool grouped_supported(const moe_weights* W) {
 
 bool block_ok(int32_t bs) { return bs == 32 || bs == 64 || bs == 128; }
 
-// Grouped-path crossover: T * slots above which expert-centric packing wins.
-// Measured on gfx950 (MXFP4 4096 x 1536 x 128 experts sweep, uniform and Zipf
-// routing); other shapes use the same per-entry threshold.
-int32_t decode_entry_threshold(const moe_weights* W) {
-  (void)W;
-  return 64 * 8;
+// Stored bytes of one expert (weights and scales of gate, up and down).
+double expert_bytes(const moe_weights* W) {
+  const double hi = (double)W->hidden * W->inter;
+  switch (W->format) {
+    case MOE_W_F32: return 3.0 * hi * 4.0;
+    case MOE_W_MXFP8: return 3.0 * hi * (1.0 + 1.0 / 32);
+    case MOE_W_MXFP4: return 3.0 * hi * (0.5 + 1.0 / 32);
+    default: return 3.0 * hi * (1.0 + 4.0 / (128.0 * 128.0));
+  }
+}
+
+// Regime choice: output-centric decode for small batches, expert-centric
+// packing beyond (the warp-decode post's section on Composer).  Both costs
+// are modelled in microseconds with constants fitted to MI355X sweeps of both
+// paths over the Qwen3 (MXFP8), DeepSeek-V3 (FP8 128x128) and MXFP4 layers:
+//  decode : the touched experts' bytes at 4.5 TB/s and VALU work of
+//           1.35e-7 us per (token, slot) entry per H*I overlap, with 30% of
+//           the smaller of the two showing through, plus 8 us;
+//  grouped: the same bytes at 4.3 TB/s (3.2 TB/s for E2M1 weights, whose
+//           stage rows are half cache lines) with the matrix work hidden,
+//           plus 45 us for sort, gather, combine and launches.
+// The touched experts are their expectation under uniform routing; skewed
+// routing touches fewer, which favours the grouped path a little earlier
+// than this predicts.
+int32_t model_path(const moe_weights* W, int32_t T, int32_t k) {
+  const double n = W->num_experts;
+  const double p = std::min(1.0, (double)k / n);
+  const double u = n * (1.0 - std::pow(1.0 - p, (double)T)) + W->num_shared;
+  const double bytes = u * expert_bytes(W);
+  const double entries = (double)T * (k + W->num_shared);
+  const double valu = entries * W->hidden * W->inter * 1.35e-7;
+  const double mem_d = bytes / 4.5e6;
+  const double t_dec = std::max(mem_d, valu) + 0.3 * std::min(mem_d, valu) + 8.0;
+  const double t_grp = bytes / (W->format == MOE_W_MXFP4 ? 3.2e6 : 4.3e6) + 45.0;
+  return t_grp < t_dec ? MOE_PATH_GROUPED : MOE_PATH_DECODE;
 }
 
 struct GroupedLayout {
@@ -285,7 +317,7 @@ int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
   if (!grouped_supported(W)) return MOE_PATH_DECODE;
   if (W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;
   if (entries > kDecodeMaxEntries) return MOE_PATH_GROUPED;
-  return entries <= decode_entry_threshold(W) ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
+  return model_path(W, T, k);
 }
 
 size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k, int32_t path,

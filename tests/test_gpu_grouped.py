@@ -206,3 +206,23 @@ def test_grouped_layer_full_size_sampled(lib, cid, t, bs, kind):
     x64 = L.activations_f64(x[sample], cfg.act)
     ref = L.moe_layer(x64, ids[sample], w[sample], act_quant="mxfp8", **oracle_kw(cfg))
     assert_layer_close(y[sample], ref, (cid, t, bs))
+
+
+@pytest.mark.parametrize("t,want", [(8, "decode"), (200, "grouped")])
+def test_layer_auto_matches_the_oracle_mode_of_its_path(lib, t, want):
+    """moe_layer(AUTO) on the Qwen3-style layer picks output-centric decode at
+    a small batch and expert-centric packing at a large one; each result is
+    held to the oracle in the mode of the path it reports (decode: float64
+    activations; grouped: MXFP8 activations and two-term h)."""
+    cfg = W.CONFIGS[2]
+    x, ids, w = inputs(cfg, t)
+    Wd = device_weights(cfg)
+    assert lib.choose_path(Wd, t, cfg.top_k) == want
+    y, chosen = lib.layer(Wd, to_device_x(cfg, x), *device_routing(ids, w), path="auto")
+    torch.cuda.synchronize()
+    assert chosen == want
+    sample = sorted({0, t // 2, t - 1})
+    x64 = L.activations_f64(x[sample], cfg.act)
+    mode = "none" if chosen == "decode" else "mxfp8"
+    ref = L.moe_layer(x64, ids[sample], w[sample], act_quant=mode, **oracle_kw(cfg))
+    assert_layer_close(to_f64(y)[sample], ref, (t, chosen))
