@@ -561,7 +561,9 @@ hipError_t gate_up_nr(const GateUpArgs& a, int nr, bool pre, int mch, bool guard
 template <int FMT, int LPR, int CPL, bool HBF16>
 hipError_t down_launch(const DownArgs& a, bool expert_major, int ybf16, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
-  if (expert_major && a.rpl == 2)
+  if (expert_major && a.rpl == 4)
+    hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 4, HBF16>), g, b, 0, s, a);
+  else if (expert_major && a.rpl == 2)
     hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 2, HBF16>), g, b, 0, s, a);
   else if (expert_major)
     hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 1, HBF16>), g, b, 0, s, a);
@@ -711,11 +713,12 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
   const int nd = kWave / lpr;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
   const bool em_launch = slot_out != nullptr;
-  // two rows per lane group in the expert-major kernel: twice the bytes per
-  // item, each staged h chunk used twice
+  // two or four rows per lane group in the expert-major kernel: more bytes
+  // in flight per item, each staged h chunk used for every row
   const int elems = W.format == W_F32 ? 4 : W.format == W_MXFP4 ? 32 : 16;
   const int hregs = a.cpl * elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
-  a.rpl = em_launch ? env_int("MOE_TUNE_DN_RPL", 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1) : 1;
+  const int rpl_fit = 4 * a.cpl * 5 + hregs <= 96 ? 4 : 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1;
+  a.rpl = em_launch ? env_int("MOE_TUNE_DN_RPL", rpl_fit) : 1;
   a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
