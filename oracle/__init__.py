@@ -20,10 +20,15 @@ What is computed, and where it comes from:
   sections on the traditional MoE path and on how the two kernels work).
 * ``align_sort``-- the block-padded, expert-grouped ordering of (token, slot)
   entries (align-and-sort article, background section and the D-C-P section).
+* ``router``    -- the router front-end: gating scores (+ bias) -> top-k ids and
+  softmax weights over the selected scores (align-and-sort article, background
+  and FasterTransformer sections).  ``workloads`` synthesises the routing
+  *inputs* of the FFN path by its own recipe; the router kernel is checked
+  only against this module.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against library routines, exhaustive enumerations, brute force and invariants.
 No function is "parity unpinned".
 """
 
-from . import formats, layer, align_sort  # noqa: F401
+from . import formats, layer, align_sort, router  # noqa: F401

@@ -251,35 +251,44 @@ def _top_k(scores, k):
     return idx
 
 
-def routing(cfg, t, kind=None, variant=0):
-    """(topk_ids int32 [T][k], topk_weights float32 [T][k]) for the routed
-    slots; the shared expert's slot is implied, not listed."""
+def gating_scores(cfg, t, kind=None, variant=0):
+    """Gating scores of T tokens over the routed experts: (scores float32
+    [T][E], bias float32 [E] or None).  Selection uses scores + bias.
+      softmax_normal / biased: scores ~ N(0,1) (biased: bias ~ N(0, 0.5));
+      uniform: scores ~ U(0,1);
+      zipf: log p(e) + Gumbel noise with p(e) ~ rank(e)^-s over a seeded
+            permutation of ranks (top-k of these is sampling k experts without
+            replacement from the Zipf popularity)."""
     kind = kind or cfg.routing
     g = rng(cfg, STREAM_ROUTE, t, variant, {"softmax_normal": 0, "uniform": 1, "biased": 2,
                                             "zipf": 3}[kind])
-    e, k = cfg.num_experts, cfg.top_k
-    if kind == "softmax_normal":
-        logits = g.standard_normal((t, e))
-        idx = _top_k(logits, k)
-        w = _softmax(np.take_along_axis(logits, idx, axis=1))
+    e = cfg.num_experts
+    bias = None
+    if kind in ("softmax_normal", "biased"):
+        scores = g.standard_normal((t, e))
+        if kind == "biased":
+            bias = rng(cfg, STREAM_BIAS).normal(0.0, np.sqrt(0.5), size=e).astype(np.float32)
     elif kind == "uniform":
-        logits = g.random((t, e))
-        idx = _top_k(logits, k)
-        w = _softmax(np.take_along_axis(logits, idx, axis=1))
-    elif kind == "biased":
-        bias = rng(cfg, STREAM_BIAS).normal(0.0, np.sqrt(0.5), size=e)
-        logits = g.standard_normal((t, e))
-        idx = _top_k(logits + bias[None, :], k)
-        w = _softmax(np.take_along_axis(logits, idx, axis=1))
+        scores = g.random((t, e))
     elif kind == "zipf":
         s = cfg.zipf_s or 1.1
         rank = rng(cfg, STREAM_RANK).permutation(e) + 1        # hot experts scattered
         logp = -s * np.log(rank.astype(np.float64))
         scores = logp[None, :] + g.gumbel(size=(t, e))
-        idx = _top_k(scores, k)
-        w = _softmax(np.take_along_axis(scores, idx, axis=1))
     else:
         raise ValueError(kind)
+    return scores.astype(np.float32), bias
+
+
+def routing(cfg, t, kind=None, variant=0):
+    """(topk_ids int32 [T][k], topk_weights float32 [T][k]) for the routed
+    slots, synthesised from gating_scores(): the k largest scores + bias
+    (stable: ties to the lower index), weighted by a softmax over the
+    selected raw scores.  The shared expert's slot is implied, not listed."""
+    scores, bias = gating_scores(cfg, t, kind, variant)
+    key = scores if bias is None else scores + bias[None, :]
+    idx = _top_k(key, cfg.top_k)
+    w = _softmax(np.take_along_axis(scores, idx, axis=1).astype(np.float64))
     return idx.astype(np.int32), w.astype(np.float32)
 
 
