@@ -247,6 +247,9 @@ def main():
     del layers, arrays, w0
     torch.cuda.empty_cache()
 
+    router = [router_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t)
+              for cid, t in ((2, B), (3, 64), (4, 16384))]
+
     grouped = []
     if not args.no_grouped:
         # DeepSeek-V3-shaped layer at B = 256 (HBM-bound) and the Zipf
@@ -291,6 +294,7 @@ def main():
         "sweep": sweep,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "router": router,
         "grouped": grouped,
     }
     if crossover:
@@ -304,6 +308,28 @@ def _device_inputs(torch, dev, W, cfg, t, kind, variant=0):
     xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
           else torch.from_numpy(x)).to(dev)
     return xd, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), ids
+
+
+def router_report(moe, W, torch, dev, stream, cfg, t, steps=50):
+    """Router front-end (gating scores -> top-k ids and weights) timed with
+    HIP events; bytes = scores read + ids and weights written."""
+    scores, bias = W.gating_scores(cfg, t)
+    s = torch.from_numpy(scores).to(dev)
+    b = None if bias is None else torch.from_numpy(bias).to(dev)
+    for _ in range(3):
+        moe.topk_route(s, cfg.top_k, bias=b)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        moe.topk_route(s, cfg.top_k, bias=b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = scores.nbytes + (0 if bias is None else bias.nbytes) + t * cfg.top_k * 8
+    return {"workload": cfg.name, "tokens": t, "experts": cfg.num_experts, "top_k": cfg.top_k,
+            "biased": bias is not None, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
 
 
 def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmup=3):

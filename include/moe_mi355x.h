@@ -265,6 +265,33 @@ moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t 
                        void* y, int32_t y_dtype, void* stream);
 
 /* ------------------------------------------------------------------ */
+/* Router front-end (the step before the path).                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * moe_topk_route: routing from gating scores (align-and-sort article,
+ * background section: experts are activated by their top-k gating scores,
+ * with a per-expert bias added for the selection in DeepSeek V3/R1;
+ * FasterTransformer section: the fused top-k gating softmax and its biased
+ * variant).  For every token t:
+ *   key[e]             = scores[t][e] + bias[e], in float32 (bias may be NULL)
+ *   topk_ids[t][0..k)  = the experts of the k largest keys, largest first;
+ *                        equal keys go to the lower expert index
+ *   topk_weights[t][j] = exp(s_j - max s) / sum_i exp(s_i - max s) with
+ *                        s_j = scores[t][topk_ids[t][j]] (a softmax over the
+ *                        selected raw scores: the renormalised top-k of a
+ *                        softmax over all experts)
+ *   scores device [T][E] float32, bias device [E] float32 or NULL;
+ *   topk_ids device [T][k] int32 and topk_weights device [T][k] float32 are
+ *   written (caller-owned; they are the inputs of the routed-expert layer).
+ * Sizes: T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64).  Scores and bias must
+ * be finite (not checked).  Errors: MOE_ERR_INVALID_ARG for bad sizes or null
+ * pointers (nothing enqueued); T == 0 is a no-op.
+ */
+moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int32_t E,
+                          int32_t k, int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* ------------------------------------------------------------------ */
 /* The whole layer.                                                     */
 /* ------------------------------------------------------------------ */
 

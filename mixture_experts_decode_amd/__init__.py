@@ -56,6 +56,7 @@ _SIGS = {
     "moe_grouped_gate_up": (_I, [_WP, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "moe_grouped_down": (_I, [_WP, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _I, _P]),
+    "moe_topk_route": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
     "moe_choose_path": (_I, [_WP, _I, _I]),
     "moe_layer_workspace_bytes": (_Z, [_WP, _I, _I, _I, _I]),
     "moe_layer": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _Z,
@@ -256,6 +257,19 @@ def combine(slot_out, t, slots, y=None, y_dtype="f32", stream=None):
     st = _lib.moe_combine(_ptr(slot_out), t, slots, h, _ptr(y), _dt(y), _stream(stream))
     _check(st, "moe_combine")
     return y
+
+
+def topk_route(scores, k, bias=None, stream=None):
+    """Router front-end: scores [T][E] float32 (device), bias [E] or None ->
+    (topk_ids int32 [T][k], topk_weights float32 [T][k])."""
+    load()
+    t, e = scores.shape
+    ids = torch.empty((t, k), dtype=torch.int32, device=scores.device)
+    wts = torch.empty((t, k), dtype=torch.float32, device=scores.device)
+    st = _lib.moe_topk_route(_ptr(scores), None if bias is None else _ptr(bias), t, e, k, _ptr(ids),
+                             _ptr(wts), _stream(stream))
+    _check(st, "moe_topk_route")
+    return ids, wts
 
 
 def choose_path(W, t, k):

@@ -311,6 +311,17 @@ moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t 
   return from_hip(moe::launch_combine(slot_out, T, slots, H, y, y_dtype, as_stream(stream)));
 }
 
+moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int32_t E, int32_t k,
+                          int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (T < 0 || E < 1 || E > kMaxExpertsTotal || k < 1 || k > E || k > 64)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!scores || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * E > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_topk_route(scores, bias, T, E, k, topk_ids, topk_weights,
+                                         as_stream(stream)));
+}
+
 int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
   if (check_weights(W) != MOE_OK || T < 0 || k < 0) return MOE_PATH_DECODE;
   const int64_t entries = (int64_t)T * (k + W->num_shared);

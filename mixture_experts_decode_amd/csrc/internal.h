@@ -45,6 +45,8 @@ hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const ui
                                const int32_t* sorted, const int32_t* expert_ids,
                                const int32_t* npp, int capacity, int bs, const float* wts,
                                int T, int k, float* slot_out, hipStream_t s);
+hipError_t launch_topk_route(const float* scores, const float* bias, int T, int E, int k,
+                             int32_t* ids, float* wts, hipStream_t s);
 hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* y, int y_dtype,
                           hipStream_t s);
 

@@ -108,6 +108,14 @@ def test_host_argument_errors(lib):
                          None, None) == moe.ERR_INVALID_ARG
     assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 2, 48, dummy,
                          1 << 30, None, None) == moe.ERR_UNSUPPORTED
+    # router: sizes, null pointers, T == 0 is a no-op
+    assert lib.moe_topk_route(dummy, None, 4, 128, 0, dummy, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(dummy, None, 4, 128, 129, dummy, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(dummy, None, 4, 2048, 8, dummy, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(dummy, None, 4, 128, 65, dummy, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(None, None, 4, 128, 8, dummy, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(dummy, None, 4, 128, 8, dummy, None, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_topk_route(None, None, 0, 128, 8, None, None, None) == moe.OK
     # grouped steps reject fp32 weights
     assert lib.moe_grouped_gate_up(ctypes.byref(_weights(moe, format=0)), dummy, dummy, dummy, dummy,
                                    64, 64, dummy, dummy, None) == moe.ERR_UNSUPPORTED

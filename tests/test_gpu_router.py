@@ -1,0 +1,76 @@
+"""Router front-end parity on the GPU: moe_topk_route against oracle.router.
+The expert ids are compared bit-exactly (both sides decide on the same
+float32 keys); the weights to 2e-6 relative (float32 exp and division
+against float64)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import router as R
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(lib, scores, k, bias=None):
+    s = torch.from_numpy(np.ascontiguousarray(scores, dtype=np.float32)).cuda()
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).cuda()
+    ids, wts = lib.topk_route(s, k, bias=b)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), wts.cpu().numpy()
+
+
+def _check(lib, scores, k, bias=None, rows=None):
+    ids, wts = _route(lib, scores, k, bias)
+    rows = np.arange(scores.shape[0]) if rows is None else rows
+    ref_ids, ref_w = R.topk_route(scores[rows], k, bias)
+    assert np.array_equal(ids[rows], ref_ids)
+    assert np.allclose(wts[rows], ref_w, rtol=2e-6, atol=1e-8)
+    return ids, wts
+
+
+@pytest.mark.parametrize("cid,t,kind", [(2, 32, None), (2, 1, None), (3, 64, None), (5, 256, "zipf"),
+                                        (1, 4, None)])
+def test_route_workload_scores(lib, cid, t, kind):
+    cfg = W.CONFIGS[cid]
+    scores, bias = W.gating_scores(cfg, t, kind)
+    _check(lib, scores, cfg.top_k, bias)
+
+
+def test_route_prefill_full_size_sampled(lib):
+    cfg = W.CONFIGS[4]
+    scores, bias = W.gating_scores(cfg, 16384)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(16384 - 64, 16384),
+                                     np.random.default_rng(5).integers(0, 16384, 256)]))
+    ids, _ = _check(lib, scores, cfg.top_k, bias, rows=rows)
+    # every token's ids are distinct and in range
+    srt = np.sort(ids, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1]) and ids.min() >= 0 and ids.max() < cfg.num_experts
+
+
+@pytest.mark.parametrize("e,k", [(70, 1), (70, 7), (8, 8), (1, 1), (1024, 64), (513, 5), (64, 64)])
+def test_route_shapes(lib, e, k):
+    rng = np.random.default_rng(e * 100 + k)
+    scores = rng.standard_normal((37, e)).astype(np.float32)
+    bias = rng.normal(0, 0.7, e).astype(np.float32)
+    _check(lib, scores, k)
+    _check(lib, scores, k, bias)
+
+
+def test_route_ties_and_signed_zero(lib):
+    rng = np.random.default_rng(9)
+    scores = rng.integers(-2, 3, size=(200, 96)).astype(np.float32)     # heavy ties
+    _check(lib, scores, 8)
+    z = np.zeros((3, 16), dtype=np.float32)
+    z[0, ::2] = -0.0                                                      # -0 ties +0
+    z[1] = np.float32(1.5)
+    z[2, 5] = np.float32(-1.0)
+    _check(lib, z, 4)
+    bias = np.where(np.arange(96) % 3 == 0, np.float32(1.0), np.float32(0.0)).astype(np.float32)
+    _check(lib, scores, 8, bias)
+
+
+def test_route_empty_batch(lib):
+    ids, wts = _route(lib, np.zeros((0, 32), dtype=np.float32), 4)
+    assert ids.shape == (0, 4) and wts.shape == (0, 4)
