@@ -356,15 +356,31 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
                             : r32 * S::BRB + (((4 * st + 2 * q + h) ^ swz<S::BP>(r32)) << 4);
     }
 
-  for (int t = xcd * chunk + local; t < t_end; t += per_x) {
+  // per-tile state, set by setup(t) for the tile whose loads are queued
+  constexpr int AR_I = 1024 / S::ARB, BR_I = 1024 / S::BRB;   // rows per DMA instruction
+  int row0 = 0, nt = 0;
+  const uint8_t* a_base0 = g.a;
+  const uint8_t* a_base1 = g.a;
+  const uint8_t* b_base = g.b;
+  const uint8_t* sa_base0 = g.as;
+  const uint8_t* sa_base1 = g.as;
+  const uint8_t* sb_base = reinterpret_cast<const uint8_t*>(g.bs);
+  uint32_t a_src[S::A_INSTR];
+  uint32_t b_src[S::B_INSTR];
+  uint32_t sa_src[S::SA_INSTR];
+  int sa_dst[S::SA_INSTR];
+  uint32_t sb_src[S::SB_INSTR];
+
+  auto setup = [&](int t) {
     const int gsz = kGroupM * g.n_ntiles;
     const int grp = t / gsz;
     const int rem = t - grp * gsz;
     const int gm = min(kGroupM, n_mb - grp * kGroupM);
-    const int nt = rem / gm;
-    const int mb = grp * kGroupM + (rem - nt * gm);
+    nt = rem / gm;
+    // uniform by construction; said so, the expert id is a scalar load
+    const int mb = __builtin_amdgcn_readfirstlane(grp * kGroupM + (rem - nt * gm));
     const int e = g.expert_ids[mb];
-    const int row0 = mb * BM;
+    row0 = mb * BM;
     // the per-lane DMA offsets are recomputed for every tile (a few VALU
     // operations) rather than hoisted out of the tile loop and spilled
     int ln = lane;
@@ -372,30 +388,25 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
 
     // ---- DMA sources: a uniform base per operand (advanced by the stage)
     // plus a 32-bit per-lane offset that stays fixed for the whole tile
-    const uint8_t* a_base0 = g.a + (size_t)row0 * g.K;
-    const uint8_t* a_base1 = TERMS > 1 ? g.a_lo + (size_t)row0 * g.K : a_base0;
-    const uint8_t* b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
-    constexpr int AR_I = 1024 / S::ARB, BR_I = 1024 / S::BRB;   // rows per DMA instruction
-    uint32_t a_src[S::A_INSTR];
+    a_base0 = g.a + (size_t)row0 * g.K;
+    a_base1 = TERMS > 1 ? g.a_lo + (size_t)row0 * g.K : a_base0;
+    b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
       const int j = (w + 4 * i) % (BM / AR_I);
       const int row = AR_I * j + ln / S::AP;
       a_src[i] = (uint32_t)(row * g.K + (((ln % S::AP) ^ swz<S::AP>(row)) << 4));
     }
-    uint32_t b_src[S::B_INSTR];
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i) {
       const int row = BR_I * (w + 4 * i) + ln / S::BP;
       b_src[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (((ln % S::BP) ^ swz<S::BP>(row)) << 4));
     }
-    const uint8_t* sa_base0 = g.as + (size_t)row0 * k_blocks;
-    const uint8_t* sa_base1 = TERMS > 1 ? g.as_lo + (size_t)row0 * k_blocks : sa_base0;
-    const uint8_t* sb_base =
+    sa_base0 = g.as + (size_t)row0 * k_blocks;
+    sa_base1 = TERMS > 1 ? g.as_lo + (size_t)row0 * k_blocks : sa_base0;
+    sb_base =
         S::T128 ? reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * (g.rows_per_expert >> 7) * k_tiles * 4
                 : reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * g.rows_per_expert * k_blocks;
-    uint32_t sa_src[S::SA_INSTR];
-    int sa_dst[S::SA_INSTR];
 #pragma unroll
     for (int q = 0; q < S::SA_INSTR; ++q) {
       if constexpr (S::AS_COOP) {
@@ -408,7 +419,6 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
         sa_dst[q] = ((w * TERMS + tm) * S::SA + 64 * u) * 4;
       }
     }
-    uint32_t sb_src[S::SB_INSTR];
 #pragma unroll
     for (int u = 0; u < S::SB_INSTR; ++u) {
       if constexpr (S::T128) {
@@ -418,137 +428,146 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
         sb_src[u] = (uint32_t)(b_row(nt, wave_brow(i)) * k_blocks);
       }
     }
+  };
 
-    // stage s reads the scale dword holding K blocks [4 * (s*KSTEPS/2), +4)
-    auto issue = [&](int s, int buf) {
-      uint8_t* base = lds + buf * S::STAGE;
-      const int ks = s * S::KSTAGE;                   // first K element of the stage
+  // stage s reads the scale dword holding K blocks [4 * (s*KSTEPS/2), +4)
+  auto issue = [&](int s, int buf) {
+    uint8_t* base = lds + buf * S::STAGE;
+    const int ks = s * S::KSTAGE;                   // first K element of the stage
 #pragma unroll
-      for (int i = 0; i < S::A_INSTR; ++i) {
-        const int j = w + 4 * i;                      // WG instruction: plane j / (BM / AR_I)
-        const uint8_t* src = (j >= BM / AR_I ? a_base1 : a_base0) + ks;
-        dma16(src + a_src[i], base + (j / (BM / AR_I)) * BM * S::ARB + (j % (BM / AR_I)) * 1024);
+    for (int i = 0; i < S::A_INSTR; ++i) {
+      const int j = w + 4 * i;                      // WG instruction: plane j / (BM / AR_I)
+      const uint8_t* src = (j >= BM / AR_I ? a_base1 : a_base0) + ks;
+      dma16(src + a_src[i], base + (j / (BM / AR_I)) * BM * S::ARB + (j % (BM / AR_I)) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < S::B_INSTR; ++i)
+      dma16(b_base + (S::FP4 ? ks / 2 : ks) + b_src[i], base + S::A_BYTES + (w + 4 * i) * 1024);
+    const int sdw = (ks >> 7) * 4;                  // byte offset of the scale dword
+    uint8_t* as_lds = base + S::A_BYTES + S::B_BYTES;
+#pragma unroll
+    for (int q = 0; q < S::SA_INSTR; ++q) {
+      const int tm = S::AS_COOP ? q : q / (S::SA / 64);
+      dma4((tm ? sa_base1 : sa_base0) + sdw + sa_src[q], as_lds + sa_dst[q]);
+    }
+    uint8_t* bs_lds = as_lds + S::AS_BYTES + w * S::SB * 4;
+#pragma unroll
+    for (int u = 0; u < S::SB_INSTR; ++u)
+      dma4(sb_base + (S::T128 ? (ks >> 7) * 4 : sdw) + sb_src[u], bs_lds + 64 * u * 4);
+  };
+
+  // acc[m][f]: 32 weight rows of fragment f (MFMA rows) x 32 sorted rows of
+  // fragment m (MFMA columns)
+  f32x16 acc[MF][NF];
+#pragma unroll
+  for (int m = 0; m < MF; ++m)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[m][f] = f32x16{0};
+  f32x16 part[S::T128 ? MF : 1][S::T128 ? NF : 1];
+  if constexpr (S::T128) {
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
+  }
+
+  auto compute = [&](int s, int buf) {
+    const uint8_t* base = lds + buf * S::STAGE;
+    const uint8_t* at = base + wm * S::WROWS * S::ARB;
+    const uint8_t* bt = base + S::A_BYTES;
+    const uint32_t* as_lds = reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES);
+    const uint32_t* bs_lds = as_lds + S::AS_BYTES / 4 + w * S::SB;
+    uint32_t sa[TERMS][MF];
+#pragma unroll
+    for (int tm = 0; tm < TERMS; ++tm)
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        if constexpr (S::AS_COOP) sa[tm][m] = as_lds[tm * 256 + m * 64 + r32];
+        else sa[tm][m] = as_lds[(w * TERMS + tm) * S::SA + 32 * m + r32];
+      }
+    uint32_t sb[NF];
+    float tsc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if constexpr (S::T128) {
+        tsc[f] = __uint_as_float(bs_lds[f]);
+        sb[f] = 0x7f7f7f7fu;
+      } else {
+        sb[f] = bs_lds[32 * f + r32];
+      }
+    }
+    // byte of the scale dword for K step st of this stage, K block h
+    const int sbyte0 = KSTEPS == 2 ? 0 : 2 * (s & 1);
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      const int sh = 8 * (sbyte0 + 2 * st + h);
+      i32x8 bf[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const uint8_t* br = bt + wave_brow(32 * f) * S::BRB;
+        if constexpr (S::FP4) {
+          const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
+          bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], 0, 0, 0, 0};
+        } else {
+          const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
+          const u32x4 q1 = *reinterpret_cast<const u32x4*>(br + b_off[st][1]);
+          bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
+                        (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+        }
       }
 #pragma unroll
-      for (int i = 0; i < S::B_INSTR; ++i)
-        dma16(b_base + (S::FP4 ? ks / 2 : ks) + b_src[i], base + S::A_BYTES + (w + 4 * i) * 1024);
-      const int sdw = (ks >> 7) * 4;                  // byte offset of the scale dword
-      uint8_t* as_lds = base + S::A_BYTES + S::B_BYTES;
+      for (int tm = 0; tm < TERMS; ++tm) {
 #pragma unroll
-      for (int q = 0; q < S::SA_INSTR; ++q) {
-        const int tm = S::AS_COOP ? q : q / (S::SA / 64);
-        dma4((tm ? sa_base1 : sa_base0) + sdw + sa_src[q], as_lds + sa_dst[q]);
+        for (int m = 0; m < MF; ++m) {
+          const uint8_t* ar = at + tm * BM * S::ARB + m * 32 * S::ARB;
+          const u32x4 q0 = *reinterpret_cast<const u32x4*>(ar + a_off[st][0]);
+          const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a_off[st][1]);
+          const i32x8 af = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
+                            (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
+          const int sca = (int)((sa[tm][m] >> sh) & 0xffu);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const int scb = (int)((sb[f] >> sh) & 0xffu);
+            // weights as the first (row) operand, activations as the second
+            if constexpr (S::T128) {
+              part[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bf[f], af, part[m][f], 0, 0, 0, scb, 0, sca);
+            } else {
+              acc[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  bf[f], af, acc[m][f], S::FP4 ? 4 : 0, 0, 0, scb, 0, sca);
+            }
+          }
+        }
       }
-      uint8_t* bs_lds = as_lds + S::AS_BYTES + w * S::SB * 4;
+    }
+    if constexpr (S::T128) {
+      // a 128-wide K tile is complete: promote it with its float scale
+      if (KSTEPS == 2 || (s & 1)) {
 #pragma unroll
-      for (int u = 0; u < S::SB_INSTR; ++u)
-        dma4(sb_base + (S::T128 ? (ks >> 7) * 4 : sdw) + sb_src[u], bs_lds + 64 * u * 4);
-    };
+        for (int m = 0; m < MF; ++m)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], tsc[f], acc[m][f][q]);
+            part[m][f] = f32x16{0};
+          }
+      }
+    }
+  };
 
-    // acc[m][f]: 32 weight rows of fragment f (MFMA rows) x 32 sorted rows of
-    // fragment m (MFMA columns)
-    f32x16 acc[MF][NF];
+  int t = xcd * chunk + local;
+  if (t < t_end) {
+    setup(t);
+    for (int s = 0; s < min(NS - 1, nst); ++s) issue(s, s);
+  }
+  while (t < t_end) {
 #pragma unroll
     for (int m = 0; m < MF; ++m)
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[m][f] = f32x16{0};
-    f32x16 part[S::T128 ? MF : 1][S::T128 ? NF : 1];
-    if constexpr (S::T128) {
-#pragma unroll
-      for (int m = 0; m < MF; ++m)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) part[m][f] = f32x16{0};
-    }
 
-    auto compute = [&](int s, int buf) {
-      const uint8_t* base = lds + buf * S::STAGE;
-      const uint8_t* at = base + wm * S::WROWS * S::ARB;
-      const uint8_t* bt = base + S::A_BYTES;
-      const uint32_t* as_lds = reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES);
-      const uint32_t* bs_lds = as_lds + S::AS_BYTES / 4 + w * S::SB;
-      uint32_t sa[TERMS][MF];
-#pragma unroll
-      for (int tm = 0; tm < TERMS; ++tm)
-#pragma unroll
-        for (int m = 0; m < MF; ++m) {
-          if constexpr (S::AS_COOP) sa[tm][m] = as_lds[tm * 256 + m * 64 + r32];
-          else sa[tm][m] = as_lds[(w * TERMS + tm) * S::SA + 32 * m + r32];
-        }
-      uint32_t sb[NF];
-      float tsc[NF];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if constexpr (S::T128) {
-          tsc[f] = __uint_as_float(bs_lds[f]);
-          sb[f] = 0x7f7f7f7fu;
-        } else {
-          sb[f] = bs_lds[32 * f + r32];
-        }
-      }
-      // byte of the scale dword for K step st of this stage, K block h
-      const int sbyte0 = KSTEPS == 2 ? 0 : 2 * (s & 1);
-#pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        const int sh = 8 * (sbyte0 + 2 * st + h);
-        i32x8 bf[NF];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint8_t* br = bt + wave_brow(32 * f) * S::BRB;
-          if constexpr (S::FP4) {
-            const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
-            bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3], 0, 0, 0, 0};
-          } else {
-            const u32x4 q0 = *reinterpret_cast<const u32x4*>(br + b_off[st][0]);
-            const u32x4 q1 = *reinterpret_cast<const u32x4*>(br + b_off[st][1]);
-            bf[f] = i32x8{(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
-                          (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-          }
-        }
-#pragma unroll
-        for (int tm = 0; tm < TERMS; ++tm) {
-#pragma unroll
-          for (int m = 0; m < MF; ++m) {
-            const uint8_t* ar = at + tm * BM * S::ARB + m * 32 * S::ARB;
-            const u32x4 q0 = *reinterpret_cast<const u32x4*>(ar + a_off[st][0]);
-            const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a_off[st][1]);
-            const i32x8 af = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
-                              (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-            const int sca = (int)((sa[tm][m] >> sh) & 0xffu);
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-              const int scb = (int)((sb[f] >> sh) & 0xffu);
-              // weights as the first (row) operand, activations as the second
-              if constexpr (S::T128) {
-                part[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bf[f], af, part[m][f], 0, 0, 0, scb, 0, sca);
-              } else {
-                acc[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bf[f], af, acc[m][f], S::FP4 ? 4 : 0, 0, 0, scb, 0, sca);
-              }
-            }
-          }
-        }
-      }
-      if constexpr (S::T128) {
-        // a 128-wide K tile is complete: promote it with its float scale
-        if (KSTEPS == 2 || (s & 1)) {
-#pragma unroll
-          for (int m = 0; m < MF; ++m)
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-#pragma unroll
-              for (int q = 0; q < 16; ++q) acc[m][f][q] = fmaf(part[m][f][q], tsc[f], acc[m][f][q]);
-              part[m][f] = f32x16{0};
-            }
-        }
-      }
-    };
-
-    // ---- pipeline: NS-1 stages in flight
-    wait_vmem<0>();       // the previous tile's stores
-    wg_barrier();         // and every wavefront is done reading its buffers
-    const int pro = min(NS - 1, nst);
-    for (int s = 0; s < pro; ++s) issue(s, s);
+    // ---- pipeline: NS-1 stages in flight (the first ones were queued
+    // before the previous tile's epilogue)
     int buf = 0;
     for (int s = 0; s < nst; ++s) {
       if (s + NS - 1 <= nst) wait_vmem<(NS - 2) * S::L>();
@@ -562,10 +581,35 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
       buf = buf + 1 == NS ? 0 : buf + 1;
     }
 
+    // ---- next tile: its first stages are queued before this tile's
+    // epilogue, which then overlaps them.  Epilogue values that come from
+    // memory are read first: vector memory completes in issue order, so a
+    // later wait for them would also wait for the queued stages.
+    const int tile_row0 = row0, tile_nt = nt;
+    int ent[GATEUP ? 1 : MF];
+    float wgt[GATEUP ? 1 : MF];
+    if constexpr (!GATEUP) {
+#pragma unroll
+      for (int m = 0; m < MF; ++m) ent[m] = g.sorted[row0 + wm * S::WROWS + m * 32 + r32];
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        const bool real = ent[m] >= 0 && ent[m] < g.sentinel;
+        const int tk = real ? ent[m] / g.slots : 0, j = real ? ent[m] - tk * g.slots : 0;
+        wgt[m] = real && j < g.k ? g.wts[tk * g.k + j] : 1.0f;
+      }
+    }
+    wait_vmem<0>();      // the epilogue's inputs have arrived (nothing else is queued)
+    const int tn = t + per_x;
+    wg_barrier();        // every wavefront is done reading this tile's buffers
+    if (tn < t_end) {
+      setup(tn);
+      for (int s = 0; s < min(NS - 1, nst); ++s) issue(s, s);
+    }
+
     // ---- epilogue.  Register q of acc[m][f] holds weight row
     // 8*(q/4) + 4*h + q%4 of fragment f for sorted row r32 of fragment m, so a
     // lane owns 16 outputs of one row: four runs of 4 consecutive columns.
-    const int rbase = row0 + wm * S::WROWS;
+    const int rbase = tile_row0 + wm * S::WROWS;
     if constexpr (GATEUP) {
 #pragma unroll
       for (int m = 0; m < MF; ++m) {
@@ -573,7 +617,7 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
 #pragma unroll
         for (int f = 0; f < NF / 2; ++f) {
           // 32 neurons = one MX block of h, split over this lane and lane ^ 32
-          const int n0 = nt * (BN / 2) + wn * (S::WCOLS / 2) + 32 * f;
+          const int n0 = tile_nt * (BN / 2) + wn * (S::WCOLS / 2) + 32 * f;
           float hv[16];
           float amax = 0.0f;
 #pragma unroll
@@ -621,29 +665,26 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     } else {
 #pragma unroll
       for (int m = 0; m < MF; ++m) {
-        const int row = rbase + m * 32 + r32;
-        const int ent = g.sorted[row];
-        if (ent < 0 || ent >= g.sentinel) continue;
-        const int tk = ent / g.slots, j = ent - tk * g.slots;
-        const float wgt = j < g.k ? g.wts[tk * g.k + j] : 1.0f;
-        float* out = g.out + (size_t)ent * g.H;
+        if (ent[m] < 0 || ent[m] >= g.sentinel) continue;
+        float* out = g.out + (size_t)ent[m] * g.H;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const int c0 = nt * BN + wn * S::WCOLS + 32 * f + 4 * h;
+          const int c0 = tile_nt * BN + wn * S::WCOLS + 32 * f + 4 * h;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (c0 + 8 * r < g.N) {
               float4 v;
-              v.x = __fmul_rn(acc[m][f][4 * r + 0], wgt);
-              v.y = __fmul_rn(acc[m][f][4 * r + 1], wgt);
-              v.z = __fmul_rn(acc[m][f][4 * r + 2], wgt);
-              v.w = __fmul_rn(acc[m][f][4 * r + 3], wgt);
+              v.x = __fmul_rn(acc[m][f][4 * r + 0], wgt[m]);
+              v.y = __fmul_rn(acc[m][f][4 * r + 1], wgt[m]);
+              v.z = __fmul_rn(acc[m][f][4 * r + 2], wgt[m]);
+              v.w = __fmul_rn(acc[m][f][4 * r + 3], wgt[m]);
               *reinterpret_cast<float4*>(out + c0 + 8 * r) = v;
             }
           }
         }
       }
     }
+    t = tn;
   }
 }
 

@@ -66,7 +66,8 @@ def _blocks_for(lib, ids, n_exp, bs):
     return sort
 
 
-@pytest.mark.parametrize("fmt,bs", [("mxfp8", 64), ("mxfp8", 128), ("mxfp8", 32),
+@pytest.mark.parametrize("fmt,bs", [("mxfp8", 64), ("mxfp8", 128), ("mxfp8", 32), ("mxfp4", 128),
+                                    ("mxfp4", 32), ("fp8_blk128", 128),
                                     ("mxfp4", 64), ("fp8_blk128", 32), ("fp8_blk128", 64)])
 def test_grouped_gate_up_alone(lib, fmt, bs):
     """a7 on generator-made MXFP8 rows: h = SiLU(Wg a) * (Wu a) per block's
@@ -95,9 +96,12 @@ def test_grouped_gate_up_alone(lib, fmt, bs):
         wg, wu, _ = L.dequant_expert(cfg.fmt, get(int(e)))
         rows = slice(b * bs, (b + 1) * bs)
         want[rows] = L.silu(a[rows] @ wg.T) * (a[rows] @ wu.T)
-    # against the oracle's own two-term form of its float64 h
+    # against the oracle's own two-term form of its float64 h: each side is
+    # within half a lo step of its own h (<= 2^-9 of the element, 2^-6 of the
+    # block maximum), and where accumulation noise flips a hi code the two lo
+    # terms differ too, so a row may reach about 2 * 2^-9
     m = metrics(got, F.fake_quant_mx_e4m3_two_term(want))
-    assert m["min_cos"] > 0.99999 and m["max_rel_l2"] < 2e-3, m
+    assert m["min_cos"] > 0.99999 and m["max_rel_l2"] < 4e-3, m
     # against the unquantised h: the lo term's own MX step (~2e-3 relative)
     m = metrics(got, want)
     assert m["min_cos"] > 0.99998 and m["max_rel_l2"] < 6e-3, m
@@ -109,7 +113,8 @@ def test_grouped_gate_up_alone(lib, fmt, bs):
     assert np.mean(hq_np[0, :npp] == ch) > 0.99
 
 
-@pytest.mark.parametrize("fmt,bs", [("mxfp8", 64), ("mxfp4", 128), ("fp8_blk128", 64),
+@pytest.mark.parametrize("fmt,bs", [("mxfp8", 64), ("mxfp4", 128), ("fp8_blk128", 64), ("mxfp8", 128),
+                                    ("mxfp8", 32), ("mxfp4", 64),
                                     ("fp8_blk128", 128)])
 def test_grouped_down_alone(lib, fmt, bs):
     """a8 on generator-made two-term MXFP8 h: slot_out[i] = w_i * Wd (hi + lo)
@@ -173,6 +178,7 @@ def _grouped_layer(lib, cfg, t, bs, kind=None):
 
 
 @pytest.mark.parametrize("fmt,t,bs", [("mxfp8", 40, 64), ("mxfp4", 33, 32), ("fp8_blk128", 21, 32),
+                                      ("fp8_blk128", 150, 128), ("mxfp4", 170, 128), ("mxfp8", 1, 32),
                                       ("mxfp8", 300, 128)])
 def test_grouped_layer_small(lib, fmt, t, bs):
     cfg = SMALL[fmt]
