@@ -516,11 +516,22 @@ int env_int(const char* name, int dflt) {
 
 // ---- dispatch ------------------------------------------------------------
 
+// Shapes the launch rules below can pick (two neurons per wavefront only
+// while a row is at most two chunks per lane, BF16 rows only up to four);
+// nothing else is compiled.
+template <int NR, int MCH, bool PRE>
+constexpr bool gate_up_shape_ok() { return (NR == 1 || MCH <= 2) && (!PRE || MCH <= 4); }
+
 template <int FMT, int NR, bool PRE, bool XF32, bool HBF16>
 hipError_t gate_up_mch(const GateUpArgs& a, int mch, bool guard, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
-#define MOE_GU(M, G) \
-  hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G>), g, b, 0, s, a)
+#define MOE_GU(M, G)                                                                         \
+  do {                                                                                       \
+    if constexpr (gate_up_shape_ok<NR, M, PRE>())                                            \
+      hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G>), g, b, 0, s, a); \
+    else                                                                                     \
+      return hipErrorNotSupported;                                                           \
+  } while (0)
   if (!guard) {
     switch (mch) {
       case 1: MOE_GU(1, false); break;
@@ -561,11 +572,21 @@ hipError_t gate_up_nr(const GateUpArgs& a, int nr, bool pre, int mch, bool guard
 template <int FMT, int LPR, int CPL, bool HBF16>
 hipError_t down_launch(const DownArgs& a, bool expert_major, int ybf16, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
-  if (expert_major && a.rpl == 4)
-    hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 4, HBF16>), g, b, 0, s, a);
-  else if (expert_major && a.rpl == 2)
-    hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 2, HBF16>), g, b, 0, s, a);
-  else if (expert_major)
+  // rows per lane group as the register rule allows (4 up to 3 chunks per
+  // lane, 2 up to 4); nothing wider is compiled
+  if constexpr (CPL <= 3) {
+    if (expert_major && a.rpl == 4) {
+      hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 4, HBF16>), g, b, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (CPL <= 4) {
+    if (expert_major && a.rpl == 2) {
+      hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 2, HBF16>), g, b, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (expert_major)
     hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 1, HBF16>), g, b, 0, s, a);
   else if (ybf16)
     hipLaunchKernelGGL((down_token_kernel<FMT, LPR, CPL, HBF16, true>), g, b, 0, s, a);
@@ -629,9 +650,9 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
   if (lane_chunks > 8) return hipErrorNotSupported;
   // neurons per wavefront: two while the rows stay small in registers; rows
   // converted to BF16 once per item while that takes at most 64 VGPRs
-  const int nr = env_int("MOE_TUNE_GU_NR", mch <= 2 ? 2 : 1);
+  const int nr = mch <= 2 ? env_int("MOE_TUNE_GU_NR", 2) == 1 ? 1 : 2 : 1;
   const int elems = W.format == W_MXFP4 ? 32 : 16;
-  const bool pre = W.format != W_F32 &&
+  const bool pre = W.format != W_F32 && mch <= 4 &&
                    env_int("MOE_TUNE_GU_PRE", 2 * nr * mch * elems / 2 <= 64 ? 1 : 0) != 0;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
   a.n_groups = (W.inter + nr - 1) / nr;
@@ -718,7 +739,8 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
   const int elems = W.format == W_F32 ? 4 : W.format == W_MXFP4 ? 32 : 16;
   const int hregs = a.cpl * elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
   const int rpl_fit = 4 * a.cpl * 5 + hregs <= 96 ? 4 : 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1;
-  a.rpl = em_launch ? env_int("MOE_TUNE_DN_RPL", rpl_fit) : 1;
+  const int rpl_max = a.cpl <= 3 ? 4 : a.cpl <= 4 ? 2 : 1;   // compiled shapes
+  a.rpl = em_launch ? std::min(env_int("MOE_TUNE_DN_RPL", rpl_fit), rpl_max) : 1;
   a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
