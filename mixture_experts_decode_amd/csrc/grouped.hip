@@ -168,7 +168,7 @@ hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* 
 // ---------------------------------------------------------------------------
 // grouped GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4
 //
-// A workgroup of 4 wavefronts computes a BM x BN tile: BM sorted rows (one
+// A workgroup of 4 or 8 wavefronts computes a BM x BN tile: BM sorted rows (one
 // align-sort block, hence one expert) against BN weight rows.  Both operand
 // tiles travel HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4),
 // in NS stages of 64 * KSTEPS K, so NS-1 stages are in flight while one is
@@ -191,7 +191,6 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmBlock = 256;          // 4 wavefronts
 constexpr int kLdsBytes = 160 * 1024;    // gfx950 LDS per workgroup
 constexpr int kGroupM = 4;               // M-blocks per raster group
 
@@ -278,30 +277,32 @@ struct GemmShape {
   // activation scales: shared by the workgroup when every wavefront covers
   // all BM = 128 rows (wavefront w loads rows 32w..32w+31 into a 64-dword
   // slot, upper half duplicated), else one slice per wavefront of its rows
-  static constexpr bool AS_COOP = WM == 1 && BM == 128;
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr bool AS_COOP = WM == 1 && BM == 128 && WAVES == 4;
   static constexpr int SA = WROWS < 64 ? 64 : WROWS;
-  static constexpr int AS_BYTES = AS_COOP ? TERMS * 4 * 64 * 4 : 4 * TERMS * SA * 4;
+  static constexpr int AS_BYTES = AS_COOP ? TERMS * 4 * 64 * 4 : WAVES * TERMS * SA * 4;
   static constexpr int SB = T128 ? 64 : (WCOLS < 64 ? 64 : WCOLS);   // per wavefront
-  static constexpr int BS_BYTES = 4 * SB * 4;
+  static constexpr int BS_BYTES = WAVES * SB * 4;
   static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   static constexpr int NS_FIT = kLdsBytes / STAGE;
   static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
-  static constexpr int A_INSTR = A_BYTES / 4096;   // per wavefront
-  static constexpr int B_INSTR = B_BYTES / 4096;
+  static constexpr int A_INSTR = A_BYTES / 1024 / WAVES;   // per wavefront
+  static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
   static constexpr int SA_INSTR = AS_COOP ? TERMS : TERMS * (SA / 64);
   static constexpr int SB_INSTR = SB / 64;
   static constexpr int L = A_INSTR + B_INSTR + SA_INSTR + SB_INSTR;   // DMA ops per stage
   static_assert(KSTEPS == 1 || KSTEPS == 2, "stage depth");
-  static_assert(WM * WN == 4, "four wavefronts");
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight wavefronts");
   static_assert(WROWS % 32 == 0 && WCOLS % 32 == 0, "whole fragments");
   static_assert(!GATEUP || NF % 2 == 0, "gate and up fragments pair up");
-  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole DMA rounds");
+  static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "whole DMA rounds");
   static_assert(NS >= 2, "double buffering fits");
   static_assert((NS - 2) * L < 64, "vmcnt range");
 };
 
 template <int BFMT, bool GATEUP, int BM, int BN, int WM, int WN, int KSTEPS>
-__global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmArgs g) {
   using S = GemmShape<BFMT, GATEUP, BM, BN, WM, WN, KSTEPS>;
   constexpr int MF = S::MF, NF = S::NF, TERMS = S::TERMS, NS = S::NS;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * S::STAGE];
@@ -393,13 +394,13 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
-      const int j = (w + 4 * i) % (BM / AR_I);
+      const int j = (w + S::WAVES * i) % (BM / AR_I);
       const int row = AR_I * j + ln / S::AP;
       a_src[i] = (uint32_t)(row * g.K + (((ln % S::AP) ^ swz<S::AP>(row)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i) {
-      const int row = BR_I * (w + 4 * i) + ln / S::BP;
+      const int row = BR_I * (w + S::WAVES * i) + ln / S::BP;
       b_src[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (((ln % S::BP) ^ swz<S::BP>(row)) << 4));
     }
     sa_base0 = g.as + (size_t)row0 * k_blocks;
@@ -436,13 +437,13 @@ __global__ __launch_bounds__(kGemmBlock) void grouped_gemm_kernel(const GemmArgs
     const int ks = s * S::KSTAGE;                   // first K element of the stage
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
-      const int j = w + 4 * i;                      // WG instruction: plane j / (BM / AR_I)
+      const int j = w + S::WAVES * i;               // WG instruction: plane j / (BM / AR_I)
       const uint8_t* src = (j >= BM / AR_I ? a_base1 : a_base0) + ks;
       dma16(src + a_src[i], base + (j / (BM / AR_I)) * BM * S::ARB + (j % (BM / AR_I)) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i)
-      dma16(b_base + (S::FP4 ? ks / 2 : ks) + b_src[i], base + S::A_BYTES + (w + 4 * i) * 1024);
+      dma16(b_base + (S::FP4 ? ks / 2 : ks) + b_src[i], base + S::A_BYTES + (w + S::WAVES * i) * 1024);
     const int sdw = (ks >> 7) * 4;                  // byte offset of the scale dword
     uint8_t* as_lds = base + S::A_BYTES + S::B_BYTES;
 #pragma unroll
@@ -701,14 +702,20 @@ hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
   do {                                                                                      \
     a.n_ntiles = (GATEUP ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);            \
     hipLaunchKernelGGL((grouped_gemm_kernel<BFMT, GATEUP, BM, BN, WM, WN, KS>), dim3(grid), \
-                       dim3(kGemmBlock), 0, s, a);                                          \
+                       dim3(64 * WM * WN), 0, s, a);                                        \
   } while (0)
   if (bs == 32) {
     MOE_GG(32, 256, 1, 4, 2);
   } else if (bs == 64) {
     MOE_GG(64, 256, 1, 4, 2);
-  } else {
+  } else if constexpr (GATEUP) {
     MOE_GG(128, 256, 2, 2, 2);
+  } else {
+    // the down product reads two activation planes per weight row: eight
+    // wavefronts keep more loads in flight from L2 (measured 13 -> 18 TB/s
+    // for L2-resident streams) and interleave two waves per SIMD; gate_up's
+    // 64 x 64 wave tiles would raise its LDS operand traffic instead
+    MOE_GG(128, 256, 2, 4, 2);
   }
 #undef MOE_GG
   return hipGetLastError();
