@@ -259,13 +259,16 @@ def combine(slot_out, t, slots, y=None, y_dtype="f32", stream=None):
     return y
 
 
-def topk_route(scores, k, bias=None, stream=None):
+def topk_route(scores, k, bias=None, ids=None, wts=None, stream=None):
     """Router front-end: scores [T][E] float32 (device), bias [E] or None ->
-    (topk_ids int32 [T][k], topk_weights float32 [T][k])."""
+    (topk_ids int32 [T][k], topk_weights float32 [T][k]), written into ids /
+    wts when given."""
     load()
     t, e = scores.shape
-    ids = torch.empty((t, k), dtype=torch.int32, device=scores.device)
-    wts = torch.empty((t, k), dtype=torch.float32, device=scores.device)
+    if ids is None:
+        ids = torch.empty((t, k), dtype=torch.int32, device=scores.device)
+    if wts is None:
+        wts = torch.empty((t, k), dtype=torch.float32, device=scores.device)
     st = _lib.moe_topk_route(_ptr(scores), None if bias is None else _ptr(bias), t, e, k, _ptr(ids),
                              _ptr(wts), _stream(stream))
     _check(st, "moe_topk_route")

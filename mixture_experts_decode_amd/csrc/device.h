@@ -183,6 +183,24 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Maximum over the whole wave (unsigned), every lane gets it: DPP row
+// rotations, then the row swaps across rows, as wave_sum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0x128>(x));
+  x = max(x, dpp_u32<0x124>(x));
+  x = max(x, dpp_u32<0x122>(x));
+  x = max(x, dpp_u32<0x121>(x));
+  auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)r16[0], (uint32_t)r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+
 // Sum over each half wave (two DPP rows); every lane of the half gets it.
 __device__ __forceinline__ float half32_sum(float x) {
   x = row16_sum(x);

@@ -10,7 +10,7 @@
 // One wavefront per token.  Lane l holds experts l, l + 64, ... as 64-bit
 // candidates ordered like (key, -index): the key's bits mapped to an unsigned
 // order in the high word, the complement of the index in the low word.  Each
-// of the k rounds takes a wave maximum (xor butterfly) and retires the winner
+// of the k rounds takes a wave maximum (DPP and row swaps) and retires the winner
 // in its owner lane.  Lane j then keeps winner j and its score for the
 // softmax, which subtracts the selected maximum and sums with a wave
 // reduction.
@@ -24,21 +24,20 @@ namespace {
 
 constexpr int kRouteBlock = 256;
 
+// Wave maximum of 64-bit (key, index) candidates: the largest key word,
+// then the largest index word among the lanes holding it.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
 }
 
+// Wave maximum of a float (finite or -inf inputs), every lane gets it.
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t m = wave_max_u32(o);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
 }
 
 // Monotone map of a finite float to uint32 (-0 and +0 map alike).
@@ -81,9 +80,7 @@ __global__ __launch_bounds__(kRouteBlock) void topk_route_kernel(
   const float s = mine >= 0 ? row[mine] : -INFINITY;
   const float m = wave_max_f32(s);
   const float p = mine >= 0 ? expf(s - m) : 0.0f;
-  float sum = p;
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk);
+  const float sum = wave_sum(p);
   if (mine >= 0) {
     ids[(size_t)t * k + lane] = mine;
     wts[(size_t)t * k + lane] = p / sum;
