@@ -18,18 +18,21 @@
 extern "C" {
 #endif
 
-/* dst[0:bytes) = src[0:bytes) with 16-byte non-temporal loads and stores,
- * grid sized to fill every compute unit.  bytes must be a multiple of 16 and
- * both pointers 16-byte aligned. */
+/* dst[0:bytes) = src[0:bytes): one 16-byte load and store per thread over a
+ * grid that covers the buffer.  bytes must be a multiple of 16 and both
+ * pointers 16-byte aligned; MOE_ERR_UNSUPPORTED past (2^31-1)*256
+ * elements (the same limit holds for the read and the fill below). */
 moe_status moe_util_copy(const void* src, void* dst, size_t bytes, void* stream);
 
-/* Reads src[0:bytes) (16-byte non-temporal loads) and writes one float per
- * workgroup to sink[0:moe_util_read_sink_len()) so the loads are live. */
+/* Reads src[0:bytes) (one 16-byte load per thread) and may write one float
+ * per workgroup to sink[0:moe_util_read_sink_len()) (index taken modulo that
+ * length), a store that depends on the loaded words so the loads stay live. */
 moe_status moe_util_read(const void* src, size_t bytes, float* sink, void* stream);
 int32_t moe_util_read_sink_len(void);
 
-/* Writes `value` to every 32-bit word of dst[0:bytes): evicts caches between
- * timed calls.  bytes must be a multiple of 16. */
+/* Writes `value` to every 32-bit word of dst[0:bytes), one 16-byte store per
+ * thread: evicts caches between timed calls.  bytes must be a multiple of 16
+ * and dst 16-byte aligned. */
 moe_status moe_util_fill(void* dst, size_t bytes, uint32_t value, void* stream);
 
 /* Compute units of the current device (cached). */

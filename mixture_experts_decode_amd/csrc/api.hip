@@ -22,6 +22,10 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// the measurement kernels give each 16-byte element its own thread, in at
+// most 2^31-1 workgroups of 256
+constexpr size_t kUtilMaxElems = size_t(0x7fffffff) * 256;
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 moe_status from_hip(hipError_t e) {
@@ -404,11 +408,13 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
 
 moe_status moe_util_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst || bytes % 16 || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (bytes / 16 > kUtilMaxElems) return MOE_ERR_UNSUPPORTED;
   return from_hip(moe::launch_copy(src, dst, bytes, as_stream(stream)));
 }
 
 moe_status moe_util_read(const void* src, size_t bytes, float* sink, void* stream) {
   if (!src || !sink || bytes % 16 || !aligned16(src)) return MOE_ERR_INVALID_ARG;
+  if (bytes / 16 > kUtilMaxElems) return MOE_ERR_UNSUPPORTED;
   return from_hip(moe::launch_read(src, bytes, sink, as_stream(stream)));
 }
 
@@ -416,6 +422,7 @@ int32_t moe_util_read_sink_len(void) { return moe::kReadSinkLen; }
 
 moe_status moe_util_fill(void* dst, size_t bytes, uint32_t value, void* stream) {
   if (!dst || bytes % 16 || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (bytes / 16 > kUtilMaxElems) return MOE_ERR_UNSUPPORTED;
   return from_hip(moe::launch_fill(dst, bytes, value, as_stream(stream)));
 }
 

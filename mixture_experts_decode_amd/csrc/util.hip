@@ -14,57 +14,38 @@ namespace {
 
 constexpr int kUtilBlock = 256;
 
+// One 16-byte element per thread over a grid that covers the buffer: every
+// wavefront issues one load (and one store) and retires, which keeps the most
+// requests in flight (measured on MI355X: 6.1 TB/s read + write for 2 GiB,
+// against 4.7 TB/s for a grid-stride loop and 5.0 TB/s for a device memcpy).
 __global__ __launch_bounds__(kUtilBlock) void copy_kernel(const u32x4* __restrict__ src,
                                                           u32x4* __restrict__ dst, size_t n) {
-  size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * kUtilBlock;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 a = __builtin_nontemporal_load(src + i);
-    u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    __builtin_nontemporal_store(a, dst + i);
-    __builtin_nontemporal_store(b, dst + i + stride);
-    __builtin_nontemporal_store(c, dst + i + 2 * stride);
-    __builtin_nontemporal_store(d, dst + i + 3 * stride);
-  }
-  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
+  if (i < n) dst[i] = src[i];
 }
 
 __global__ __launch_bounds__(kUtilBlock) void read_kernel(const u32x4* __restrict__ src, size_t n,
                                                           float* __restrict__ sink) {
-  size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * kUtilBlock;
-  uint32_t acc = 0;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 a = __builtin_nontemporal_load(src + i);
-    u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
-    acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
-  }
-  for (; i < n; i += stride) {
-    u32x4 a = __builtin_nontemporal_load(src + i);
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
-  }
-  // a store that depends on every loaded word keeps the loads live; it
+  const size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
+  if (i >= n) return;
+  const u32x4 a = src[i];
+  const uint32_t acc = a[0] ^ a[1] ^ a[2] ^ a[3];
+  // a store that depends on every loaded word keeps the load live; it
   // practically never fires
   if (acc == 0x9e3779b9u) sink[blockIdx.x % kReadSinkLen] = __uint_as_float(acc);
 }
 
 __global__ __launch_bounds__(kUtilBlock) void fill_kernel(u32x4* __restrict__ dst, size_t n,
                                                           uint32_t v) {
-  size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * kUtilBlock;
-  const u32x4 q = {v, v, v, v};
-  for (; i < n; i += stride) dst[i] = q;
+  const size_t i = (size_t)blockIdx.x * kUtilBlock + threadIdx.x;
+  if (i < n) dst[i] = u32x4{v, v, v, v};
 }
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 
-int stream_blocks() { return device_num_cus() * 8; }
+// blocks covering n 16-byte elements, one per thread
+unsigned cover_blocks(size_t n) { return (unsigned)((n + kUtilBlock - 1) / kUtilBlock); }
 
 }  // namespace
 
@@ -86,15 +67,17 @@ int device_num_xcds() { return 8; }
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_kernel, dim3(stream_blocks()), dim3(kUtilBlock), 0, s,
+  if ((n + kUtilBlock - 1) / kUtilBlock > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3(cover_blocks(n)), dim3(kUtilBlock), 0, s,
                      reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n);
   return hipGetLastError();
 }
 
 hipError_t launch_read(const void* src, size_t bytes, float* sink, hipStream_t s) {
   const size_t n = bytes / 16;
-  const int blocks = std::min(stream_blocks(), kReadSinkLen);
-  hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(kUtilBlock), 0, s,
+  if (n == 0) return hipSuccess;
+  if ((n + kUtilBlock - 1) / kUtilBlock > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel, dim3(cover_blocks(n)), dim3(kUtilBlock), 0, s,
                      reinterpret_cast<const u32x4*>(src), n, sink);
   return hipGetLastError();
 }
@@ -102,7 +85,8 @@ hipError_t launch_read(const void* src, size_t bytes, float* sink, hipStream_t s
 hipError_t launch_fill(void* dst, size_t bytes, uint32_t value, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(stream_blocks()), dim3(kUtilBlock), 0, s,
+  if ((n + kUtilBlock - 1) / kUtilBlock > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fill_kernel, dim3(cover_blocks(n)), dim3(kUtilBlock), 0, s,
                      reinterpret_cast<u32x4*>(dst), n, value);
   return hipGetLastError();
 }
