@@ -13,8 +13,9 @@
 //    once per call even when several tokens share an expert.  Each workgroup
 //    finds the touched experts itself from the routed ids (LDS bitmask), so
 //    no pre-pass kernel and no host sync are needed; wavefronts loop over
-//    (expert rank, neuron group) items with a static stride, prefetching the
-//    next item's rows and the next token's activation chunk.
+//    (expert rank, neuron group) items with a static stride.  Rows of up to
+//    four chunks per lane are converted to BF16 once per item and reused for
+//    every routed token; longer rows are converted per token.
 //  * down has two variants with bitwise-identical results.  In both, a row of
 //    W_down is split over LPR lanes (8 or 16) so one wavefront covers 64/LPR
 //    output rows and every dot product is reduced inside a DPP row.
@@ -125,7 +126,7 @@ __device__ __forceinline__ int select_rank(const uint32_t* mask, int n_words, in
     r -= c;
   }
   for (int i = 0; i < r; ++i) m &= m - 1;
-  return q * 32 + __ffs(m) - 1;
+  return __builtin_amdgcn_readfirstlane(q * 32 + __ffs(m) - 1);
 }
 
 // Walks the entries routed to one expert, in ascending entry order.
@@ -345,7 +346,7 @@ MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs 
   const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
   const int n_items = U * a.n_groups;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  for (int it = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); it < n_items; it += n_waves) {
+  for (int it = blockIdx.x * kWavesPerBlock + wave_in_block(); it < n_items; it += n_waves) {
     const int e = select_rank(s_mask, a.n_words, it / a.n_groups);
     const int n0 = (it % a.n_groups) * NR;
     GateRows<FMT, NR, MCH, PRE> rows;
@@ -368,18 +369,27 @@ struct DownRow {
   float s[CPL];
 };
 
+// Row d of expert e's W_down.  e is uniform, so the expert's weight and scale
+// bases are scalar; only the offset of the lane's row inside the expert (below
+// 2^31 bytes, checked at launch) is per lane, in 32-bit arithmetic.
 template <int FMT, int LPR, int CPL>
 __device__ __forceinline__ void load_down_row(DownRow<FMT, CPL>& R, const DownArgs& a, int e,
                                               int d, int gl, bool stream) {
-  const long long row = (long long)e * a.H + d;
-  const long long tile_row = (long long)e * (a.H >> 7) + (d >> 7);
-  const uint8_t* base = a.w2 + row * a.row_bytes;
+  const uint8_t* base = a.w2 + (size_t)e * a.H * a.row_bytes + (uint32_t)d * (uint32_t)a.row_bytes;
   const int scale_len = FMT == W_FP8B128 ? (a.I >> 7) : (a.I >> 5);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = gl + LPR * i;
-    R.w[i] = stream ? load_stream16(base + (size_t)c * 16) : load16(base + (size_t)c * 16);
-    R.s[i] = chunk_scale<FMT>(a.w2s, row, c, scale_len, tile_row);
+    R.w[i] = stream ? load_stream16(base + (uint32_t)c * 16) : load16(base + (uint32_t)c * 16);
+    if constexpr (FMT == W_MXFP8 || FMT == W_MXFP4) {
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.w2s) + (size_t)e * a.H * scale_len;
+      R.s[i] = e8m0_to_f32(sb[(uint32_t)d * scale_len + (FMT == W_MXFP8 ? (c >> 1) : c)]);
+    } else if constexpr (FMT == W_FP8B128) {
+      const float* sb = reinterpret_cast<const float*>(a.w2s) + (size_t)e * (a.H >> 7) * scale_len;
+      R.s[i] = sb[(d >> 7) * scale_len + (c >> 3)];
+    } else {
+      R.s[i] = 1.0f;
+    }
   }
 }
 
@@ -432,7 +442,7 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
   const int n_items = U * a.n_dgroups;
   const int n_waves = gridDim.x * kWavesPerBlock;
   float* out = reinterpret_cast<float*>(a.y);
-  for (int it = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); it < n_items; it += n_waves) {
+  for (int it = blockIdx.x * kWavesPerBlock + wave_in_block(); it < n_items; it += n_waves) {
     const int e = select_rank(s_mask, a.n_words, it / a.n_dgroups);
     const int d0 = (it % a.n_dgroups) * ND * RPL + grp;
     DownRow<FMT, CPL> rows[RPL];
@@ -462,7 +472,7 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
   constexpr int ND = kWave / LPR;
   __shared__ float s_part[64][ND];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
+  const int wv = wave_in_block();
   const int grp = lane / LPR, gl = lane % LPR;
   const int item = xcd_logical_block(blockIdx.x, gridDim.x, a.nxcd);
   const int dg = item / a.T;
@@ -509,10 +519,6 @@ int row_bytes_of(int fmt, int k_elems) {
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return v ? std::atoi(v) : dflt;
-}
 
 // ---- dispatch ------------------------------------------------------------
 
@@ -622,6 +628,12 @@ hipError_t down_shape(const DownArgs& a, int lpr, bool em, int ybf16, int blocks
 hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
                                  const int32_t* ids, int T, int k, void* h, int h_dtype,
                                  hipStream_t s) {
+  // the matrix-core kernel takes every quantised shape it can; the vector
+  // kernel below runs the rest (FP32 weights or activations, odd shapes)
+  if (env_int("MOE_TUNE_GU_MFMA", 0) != 0) {
+    const hipError_t err = launch_gate_up_mfma(W, x, x_dtype, ids, T, k, h, h_dtype, s);
+    if (err != hipErrorNotSupported) return err;
+  }
   GateUpArgs a;
   a.w13 = reinterpret_cast<const uint8_t*>(W.w13);
   a.w13s = W.w13_scale;
@@ -730,6 +742,8 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
   a.chunks = a.row_bytes / 16;
   const int lpr = down_lanes_per_row(W.format, W.inter, h_dtype);
   if (lpr == 0) return hipErrorNotSupported;
+  // row offsets inside one expert are 32-bit in the kernels
+  if ((long long)a.H * a.row_bytes >= (1ll << 32)) return hipErrorNotSupported;
   a.cpl = a.chunks / lpr;
   const int nd = kWave / lpr;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);

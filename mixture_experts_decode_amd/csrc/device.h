@@ -14,6 +14,13 @@ enum WFormat { W_F32 = 0, W_MXFP8 = 1, W_MXFP4 = 2, W_FP8B128 = 3 };
 
 constexpr int kWave = 64;
 
+// Index of the calling wavefront inside its workgroup, as a scalar: the
+// compiler cannot prove threadIdx.x / 64 uniform by itself and would keep
+// everything derived from it (row addresses, 64-bit multiplies) per lane.
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // ---------------------------------------------------------------------------
 // loads
 // ---------------------------------------------------------------------------
@@ -261,9 +268,12 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// SiLU(g) * u in FP32.
+// SiLU(g) * u in FP32: g * sigmoid(g) with the hardware reciprocal (about
+// one ulp) instead of an IEEE division, which costs a dozen instructions per
+// output.  As g -> -inf, 1 + e^-g -> inf and the reciprocal -> 0, so the
+// product goes to (signed) zero as SiLU does.
 __device__ __forceinline__ float swiglu(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------------------------
