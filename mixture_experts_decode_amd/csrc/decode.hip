@@ -628,12 +628,6 @@ hipError_t down_shape(const DownArgs& a, int lpr, bool em, int ybf16, int blocks
 hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
                                  const int32_t* ids, int T, int k, void* h, int h_dtype,
                                  hipStream_t s) {
-  // the matrix-core kernel takes every quantised shape it can; the vector
-  // kernel below runs the rest (FP32 weights or activations, odd shapes)
-  if (env_int("MOE_TUNE_GU_MFMA", 0) != 0) {
-    const hipError_t err = launch_gate_up_mfma(W, x, x_dtype, ids, T, k, h, h_dtype, s);
-    if (err != hipErrorNotSupported) return err;
-  }
   GateUpArgs a;
   a.w13 = reinterpret_cast<const uint8_t*>(W.w13);
   a.w13s = W.w13_scale;

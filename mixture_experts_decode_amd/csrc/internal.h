@@ -29,11 +29,6 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               const int32_t* ids, const float* wts, int T, int k, void* y,
                               int y_dtype, float* slot_out, hipStream_t s);
 int down_lanes_per_row(int fmt, int inter, int h_dtype);
-// decode_mfma.hip: gate_up on the matrix cores; hipErrorNotSupported for
-// shapes it does not take (the vector kernel runs those)
-hipError_t launch_gate_up_mfma(const moe_weights& W, const void* x, int x_dtype,
-                               const int32_t* ids, int T, int k, void* h, int h_dtype,
-                               hipStream_t s);
 bool down_expert_major(int T);
 
 // align_sort.hip
