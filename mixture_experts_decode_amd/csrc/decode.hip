@@ -221,24 +221,32 @@ struct GateRows {
   float s[2 * NR][MCH];
 };
 
+// The conversion multiplies by `sc`: 1 for unscaled use, or an MX block
+// scale (a power of two, so the BF16 result stays exact while it is a
+// normal BF16 number).
 template <int FMT>
-__device__ __forceinline__ void chunk_to_bf16(const u32x4 q, uint32_t* out) {
+__device__ __forceinline__ void chunk_to_bf16(const u32x4 q, uint32_t* out, float sc) {
   if constexpr (FMT == W_MXFP4) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      out[4 * d + 0] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<0>(q[d]));
-      out[4 * d + 1] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<1>(q[d]));
-      out[4 * d + 2] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<2>(q[d]));
-      out[4 * d + 3] = __builtin_bit_cast(uint32_t, fp4x2_to_bf16x2<3>(q[d]));
+      out[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[d], sc, 0));
+      out[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[d], sc, 1));
+      out[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[d], sc, 2));
+      out[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[d], sc, 3));
     }
   } else {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      out[2 * d + 0] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(q[d]));
-      out[2 * d + 1] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(q[d]));
+      out[2 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], sc, false));
+      out[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], sc, true));
     }
   }
 }
+
+// PRE rows of MX formats carry their block scale inside the converted BF16
+// values, so the per-token dot products need no scale multiply.
+template <int FMT, bool PRE>
+constexpr bool scale_folded() { return PRE && (FMT == W_MXFP8 || FMT == W_MXFP4); }
 
 // GUARD: the row has fewer than 64*MCH chunks, lanes past the end hold zeros.
 template <int FMT, int NR, int MCH, bool PRE, bool GUARD>
@@ -272,7 +280,7 @@ __device__ __forceinline__ void load_gate_rows(GateRows<FMT, NR, MCH, PRE>& R,
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
       if constexpr (PRE) {
-        chunk_to_bf16<FMT>(raw[q][m], R.w[q][m]);
+        chunk_to_bf16<FMT>(raw[q][m], R.w[q][m], scale_folded<FMT, PRE>() ? R.s[q][m] : 1.0f);
       } else {
         R.w[q][m][0] = raw[q][m][0];
         R.w[q][m][1] = raw[q][m][1];
@@ -298,25 +306,38 @@ __device__ __forceinline__ float gate_chunk_dot(GateRows<FMT, NR, MCH, PRE>& R, 
   }
 }
 
-// All MCH activation chunks of one token are requested before any is used.
-template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD>
-__device__ __forceinline__ void gate_up_pair(GateRows<FMT, NR, MCH, PRE>& R, const GateUpArgs& a,
-                                             int pe, int n0, int lane) {
+// The MCH activation chunks of token entry pe, all requested together.
+template <int FMT, int MCH, bool XF32, bool GUARD>
+__device__ __forceinline__ void load_token_x(XChunk<FMT, XF32> (&xc)[MCH], const GateUpArgs& a,
+                                             int pe, int lane) {
   const char* xrow = reinterpret_cast<const char*>(a.x) +
                      (size_t)div_slots(pe, a.slots_magic) * a.H * (XF32 ? 4 : 2);
-  XChunk<FMT, XF32> xc[MCH];
 #pragma unroll
   for (int m = 0; m < MCH; ++m) {
     const int c = lane + m * kWave;
     load_x_chunk<FMT, XF32>(xc[m], xrow, GUARD ? min(c, a.chunks - 1) : c);
   }
+}
+
+template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD>
+__device__ __forceinline__ void gate_up_pair(GateRows<FMT, NR, MCH, PRE>& R, const GateUpArgs& a,
+                                             const XChunk<FMT, XF32> (&xc)[MCH], int pe, int n0,
+                                             int lane) {
   float acc[2 * NR];
 #pragma unroll
   for (int q = 0; q < 2 * NR; ++q) {
     acc[q] = 0.f;
+    if constexpr (scale_folded<FMT, PRE>()) {
 #pragma unroll
-    for (int m = 0; m < MCH; ++m)
-      acc[q] = fmaf(gate_chunk_dot<FMT, NR, MCH, PRE, XF32>(R, q, m, xc[m]), R.s[q][m], acc[q]);
+      for (int m = 0; m < MCH; ++m)
+#pragma unroll
+        for (int i = 0; i < GateRows<FMT, NR, MCH, PRE>::kWords; ++i)
+          acc[q] = dot2_bf16(as_bf16x2(R.w[q][m][i]), as_bf16x2(xc[m].v[i]), acc[q]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MCH; ++m)
+        acc[q] = fmaf(gate_chunk_dot<FMT, NR, MCH, PRE, XF32>(R, q, m, xc[m]), R.s[q][m], acc[q]);
+    }
   }
   float out;
   if constexpr (NR == 2) {
@@ -349,13 +370,21 @@ MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs 
   for (int it = blockIdx.x * kWavesPerBlock + wave_in_block(); it < n_items; it += n_waves) {
     const int e = select_rank(s_mask, a.n_words, it / a.n_groups);
     const int n0 = (it % a.n_groups) * NR;
-    GateRows<FMT, NR, MCH, PRE> rows;
-    load_gate_rows<FMT, NR, MCH, PRE, GUARD>(rows, a, e, n0, lane);
+    // the first routed token's activations are requested together with the
+    // rows, so they arrive in the same memory round trip
     PairIter pi;
     pairs_begin(pi, s_ids, a.n_entries, e);
-    for (int pe = pairs_next(pi, s_ids, a.n_entries, e); pe >= 0;
-         pe = pairs_next(pi, s_ids, a.n_entries, e))
-      gate_up_pair<FMT, NR, MCH, PRE, XF32, HBF16, GUARD>(rows, a, pe, n0, lane);
+    int pe = pairs_next(pi, s_ids, a.n_entries, e);
+    XChunk<FMT, XF32> xc[MCH];
+    load_token_x<FMT, MCH, XF32, GUARD>(xc, a, pe, lane);
+    GateRows<FMT, NR, MCH, PRE> rows;
+    load_gate_rows<FMT, NR, MCH, PRE, GUARD>(rows, a, e, n0, lane);
+    while (true) {
+      gate_up_pair<FMT, NR, MCH, PRE, XF32, HBF16, GUARD>(rows, a, xc, pe, n0, lane);
+      pe = pairs_next(pi, s_ids, a.n_entries, e);
+      if (pe < 0) break;
+      load_token_x<FMT, MCH, XF32, GUARD>(xc, a, pe, lane);
+    }
   }
 }
 
