@@ -31,6 +31,8 @@
  *    reported by the HIP runtime returns MOE_ERR_HIP.  No exceptions, no exit.
  *  - Preconditions NOT checked (they would need a device read): expert ids in
  *    [0, num_experts); finite weights and scales; outputs not aliasing inputs.
+ *    Every kernel reads an id outside [0, num_experts) as expert 0, so such an
+ *    id never takes an access outside the caller's buffers.
  *  - The library keeps no mutable global state apart from a per-device cache
  *    of the compute-unit count; calls are thread-safe.  Calls may be captured
  *    in a HIP graph: they record kernels only.

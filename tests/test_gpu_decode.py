@@ -176,3 +176,47 @@ def test_decode_full_size_sampled(lib, cid, t, kind):
     x64 = L.activations_f64(x[sample], cfg.act)
     ref = L.moe_layer(x64, ids[sample], w[sample], **oracle_kw(cfg))
     assert_layer_close(to_f64(y)[sample], ref, (cid, t))
+
+
+def test_out_of_range_ids_read_as_expert_zero(lib):
+    """An id outside [0, E) is read as expert 0 by every kernel (documented
+    in the header); both paths then match the oracle run on the ids with
+    those entries replaced by 0."""
+    cfg = SMALL["mxfp8"]
+    t = 6
+    x, ids, w = inputs(cfg, t)
+    bad = ids.copy()
+    bad[0, 0], bad[2, 3], bad[5, 1] = cfg.num_experts, -1, cfg.num_experts + 1000
+    fixed = np.where((bad < 0) | (bad >= cfg.num_experts), 0, bad).astype(np.int32)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    x64 = L.activations_f64(x, cfg.act)
+    for path, mode in (("decode", "none"), ("grouped", "mxfp8")):
+        y, chosen = lib.layer(Wd, xd, *device_routing(bad, w), path=path, block=32)
+        torch.cuda.synchronize()
+        assert chosen == path
+        ref = L.moe_layer(x64, fixed, w, act_quant=mode, **oracle_kw(cfg))
+        assert_layer_close(to_f64(y), ref, path)
+
+
+def test_decode_at_the_entry_limit(lib):
+    """T * slots equal to moe_decode_max_entries(): the largest batch the
+    decode kernels stage on chip (Qwen3-style layer, 256 tokens x top-8);
+    sampled tokens against the oracle, and one past it is refused."""
+    cfg = W.CONFIGS[2]
+    limit = lib.load().moe_decode_max_entries()
+    t = limit // cfg.top_k
+    assert t * cfg.top_k == limit
+    x, ids, w = inputs(cfg, t)
+    Wd = device_weights(cfg)
+    y, chosen = lib.layer(Wd, to_device_x(cfg, x), *device_routing(ids, w), path="decode")
+    torch.cuda.synchronize()
+    assert chosen == "decode"
+    sample = sorted({0, 97, t - 1})
+    x64 = L.activations_f64(x[sample], cfg.act)
+    ref = L.moe_layer(x64, ids[sample], w[sample], **oracle_kw(cfg))
+    assert_layer_close(to_f64(y)[sample], ref)
+    x2, ids2, w2 = inputs(cfg, t + 1)
+    with pytest.raises(lib.MoeError) as err:
+        lib.layer(Wd, to_device_x(cfg, x2), *device_routing(ids2, w2), path="decode")
+    assert err.value.status == lib.ERR_UNSUPPORTED
