@@ -196,8 +196,8 @@ def main():
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
+        # eager pass: per-kernel HIP events on the launch stream
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        t0 = time.perf_counter()
         s0 = torch.cuda.Event(enable_timing=True)
         s1 = torch.cuda.Event(enable_timing=True)
         s0.record(stream)
@@ -205,10 +205,29 @@ def main():
             step(i, evs[i] if chosen == "decode" else None)
         s1.record(stream)
         torch.cuda.synchronize()
+        eager_ms = s0.elapsed_time(s1)
+        y_eager = y.clone()
+        # timed pass: the same K steps captured once in a HIP graph and
+        # replayed, so no host launch cost sits between the kernels (as a
+        # decode loop would run them)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s0.record(stream)
+        g.replay()
+        s1.record(stream)
+        torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         total_ms = s0.elapsed_time(s1)
+        del g
+        if not torch.equal(y, y_eager):
+            raise RuntimeError("graph replay differs from the eager steps")
         tot_bytes = sum(ins[i % n_layers]["bytes"] for i in range(steps))
         res = {"B": b, "path": chosen, "us_per_layer": total_ms * 1e3 / steps,
+               "eager_us_per_layer": eager_ms * 1e3 / steps,
                "TBps": tot_bytes / (total_ms * 1e-3) / 1e12,
                "U_mean": float(np.mean([d["U"] for d in ins])), "wall_s": wall}
         if chosen == "decode":
@@ -228,8 +247,8 @@ def main():
         for b in cfg.batches:
             r = run_steps(b, 50, 5, args.path)
             sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
-                          if k in ("B", "path", "us_per_layer", "TBps", "U_mean", "gate_up_us",
-                                   "down_us")})
+                          if k in ("B", "path", "us_per_layer", "eager_us_per_layer", "TBps",
+                                   "U_mean", "gate_up_us", "down_us")})
 
     roofline = None
     if main_res["path"] == "decode":
@@ -277,6 +296,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(main_res["us_per_layer"] / 1e3, 5),
         "us_per_layer": round(main_res["us_per_layer"], 2),
+        "eager_us_per_layer": round(main_res["eager_us_per_layer"], 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
