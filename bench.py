@@ -463,14 +463,20 @@ def crossover_sweep(moe, W, torch, dev, stream, cfg, batches=None, kinds=(None,)
                     xd, idd, wd, _ = ins[i % 4]
                     moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
                 torch.cuda.synchronize()
+                # the steps replayed from one HIP graph, as in the headline
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(steps):
+                        xd, idd, wd, _ = ins[i % 4]
+                        moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
+                torch.cuda.synchronize()
                 s0 = torch.cuda.Event(enable_timing=True)
                 s1 = torch.cuda.Event(enable_timing=True)
                 s0.record(stream)
-                for i in range(steps):
-                    xd, idd, wd, _ = ins[i % 4]
-                    moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
+                g.replay()
                 s1.record(stream)
                 torch.cuda.synchronize()
+                del g
                 row[path + "_us"] = round(s0.elapsed_time(s1) * 1e3 / steps, 2)
             print(f"[bench] crossover {row}", file=sys.stderr, flush=True)
             out.append(row)
