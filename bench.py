@@ -271,9 +271,10 @@ def main():
 
     grouped = []
     if not args.no_grouped:
-        # DeepSeek-V3-shaped layer at B = 256 (HBM-bound) and the Zipf
-        # prefill step (MFMA-bound)
-        for cid, t, bs, kind in ((3, 256, 64, None), (4, 16384, 128, "zipf")):
+        # DeepSeek-V3-shaped layer at B = 256 (HBM-bound; 32-row blocks,
+        # the fastest measured for a dozen tokens per expert) and the Zipf
+        # prefill step (MFMA-bound, 128-row blocks)
+        for cid, t, bs, kind in ((3, 256, 32, None), (4, 16384, 128, "zipf")):
             grouped.append(grouped_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t, bs, kind,
                                           steps=min(args.steps, 20)))
             torch.cuda.empty_cache()
