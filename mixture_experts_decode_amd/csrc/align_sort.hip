@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a)
   __shared__ int s_part[kPrefixBlock];
   __shared__ int s_off[kMaxExpertsTotal + 1];
   __shared__ int s_cnt[kMaxExpertsTotal];
-  __shared__ int s_scan[kPrefixBlock];
+  __shared__ int s_wtot[kPrefixBlock / kWave];
   const int tid = threadIdx.x;
   // G threads per expert, each over a contiguous run of waves
   const int G = max(1, min(kPrefixBlock / a.n_exp, 8));
@@ -120,20 +120,32 @@ __global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a)
   const int e0 = tid * per_t, e1 = min(e0 + per_t, a.n_exp);
   int local = 0;
   for (int e = e0; e < e1; ++e) local += (s_cnt[e] + a.bs - 1) / a.bs * a.bs;
-  s_scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kPrefixBlock; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  // inclusive scan of `local` over the workgroup: each wavefront scans its
+  // 64 values with lane shifts, wavefront 0 scans the wavefront totals
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  int incl = local;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
   }
-  int run = s_scan[tid] - local;
+  if (lane == kWave - 1) s_wtot[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int t = lane < kPrefixBlock / kWave ? s_wtot[lane] : 0;
+    for (int off = 1; off < kPrefixBlock / kWave; off <<= 1) {
+      const int v = __shfl_up(t, off, kWave);
+      if (lane >= off) t += v;
+    }
+    if (lane < kPrefixBlock / kWave) s_wtot[lane] = t;
+  }
+  __syncthreads();
+  incl += wid ? s_wtot[wid - 1] : 0;
+  int run = incl - local;
   for (int e = e0; e < e1; ++e) {
     s_off[e] = run;
     run += (s_cnt[e] + a.bs - 1) / a.bs * a.bs;
   }
-  if (tid == kPrefixBlock - 1) s_off[a.n_exp] = s_scan[tid];
+  if (tid == kPrefixBlock - 1) s_off[a.n_exp] = incl;
   __syncthreads();
   const int total = s_off[a.n_exp];
   for (int e = tid; e <= a.n_exp; e += kPrefixBlock) a.offsets[e] = s_off[e];
@@ -160,11 +172,8 @@ __global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a)
       if (c + r < p) a.sorted[s_off[e] + c + r] = a.n;
     }
   }
-  // per-wave bases become absolute
-  for (int q = tid; q < a.n_waves * a.n_exp; q += kPrefixBlock) {
-    const int e = q % a.n_exp;
-    a.base[q] += s_off[e];
-  }
+  // the per-wave bases stay relative to their expert's offset; the place
+  // kernel adds the offset when it loads them
 }
 
 __global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
   if (w >= a.n_waves) return;
   int* ctr = s_ctr[wl];
   const int32_t* bse = a.base + (size_t)w * a.n_exp;
-  for (int e = lane; e < a.n_exp; e += kWave) ctr[e] = bse[e];
+  for (int e = lane; e < a.n_exp; e += kWave) ctr[e] = bse[e] + a.offsets[e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   const int lo = w * a.per_wave;
