@@ -17,7 +17,11 @@
 //    entry index inside every expert's run.
 // Cross-workgroup data goes through L2 between launches (gfx950 has no
 // on-chip workgroup-to-workgroup exchange; the article's CK/AITER section
-// notes the same of CDNA3).
+// notes the same of CDNA3).  Up to 8192 entries one workgroup runs all three
+// phases with the exchange in LDS (as_fused_kernel): one launch instead of
+// three, the same results.
+
+#include <algorithm>
 
 #include "device.h"
 #include "internal.h"
@@ -30,6 +34,8 @@ constexpr int kAsBlock = 256;
 constexpr int kAsWaves = kAsBlock / kWave;
 constexpr int kMaxWaves = 128;        // count/place wavefronts per call
 constexpr int kPrefixBlock = 1024;
+constexpr int kFusedWaves = kPrefixBlock / kWave;       // 16
+constexpr int kFusedMaxEntries = kFusedWaves * 8 * kWave;   // 8192
 
 struct AsArgs {
   const int32_t* ids;
@@ -75,46 +81,14 @@ __global__ __launch_bounds__(kAsBlock) void as_count_kernel(const AsArgs a) {
   for (int e = lane; e < a.n_exp; e += kWave) out[e] = h[e];
 }
 
-// One workgroup: per-expert merge over waves, alignment, expert scan.
-__global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a) {
-  __shared__ int s_part[kPrefixBlock];
-  __shared__ int s_off[kMaxExpertsTotal + 1];
-  __shared__ int s_cnt[kMaxExpertsTotal];
-  __shared__ int s_wtot[kPrefixBlock / kWave];
+// From the per-expert counts in s_cnt: pad every count to the block size,
+// scan over experts into s_off (and s_off[n_exp] = total), then write the
+// offsets, the padded total, the block -> expert map and the sentinel tails.
+// Whole workgroup of kPrefixBlock threads; two barriers inside, s_off
+// complete on return.
+__device__ __forceinline__ void layout_phase(const AsArgs& a, const int* s_cnt, int* s_off,
+                                             int* s_wtot) {
   const int tid = threadIdx.x;
-  // G threads per expert, each over a contiguous run of waves
-  const int G = max(1, min(kPrefixBlock / a.n_exp, 8));
-  const int per = (a.n_waves + G - 1) / G;
-
-  for (int base_e = 0; base_e < a.n_exp; base_e += kPrefixBlock / G) {
-    const int e = base_e + tid / G;
-    const int g = tid % G;
-    const bool act = tid / G < kPrefixBlock / G && e < a.n_exp;
-    const int w0 = g * per, w1 = min(w0 + per, a.n_waves);
-    int sum = 0;
-    if (act)
-      for (int w = w0; w < w1; ++w) sum += a.hist[(size_t)w * a.n_exp + e];
-    s_part[tid] = sum;
-    __syncthreads();
-    if (act) {
-      int pre = 0, tot = 0;
-      for (int q = 0; q < G; ++q) {
-        const int v = s_part[(tid / G) * G + q];
-        if (q < g) pre += v;
-        tot += v;
-      }
-      if (g == 0) s_cnt[e] = tot;
-      // exclusive base of each wave within the expert (offset added later)
-      int run = pre;
-      for (int w = w0; w < w1; ++w) {
-        const int c = a.hist[(size_t)w * a.n_exp + e];
-        a.base[(size_t)w * a.n_exp + e] = run;
-        run += c;
-      }
-    }
-    __syncthreads();
-  }
-
   // padded counts, exclusive scan over experts (blocked: thread handles a run)
   const int per_t = (a.n_exp + kPrefixBlock - 1) / kPrefixBlock;
   const int e0 = tid * per_t, e1 = min(e0 + per_t, a.n_exp);
@@ -172,9 +146,54 @@ __global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a)
       if (c + r < p) a.sorted[s_off[e] + c + r] = a.n;
     }
   }
+}
+
+// One workgroup: per-expert merge over waves, alignment, expert scan.
+__global__ __launch_bounds__(kPrefixBlock) void as_prefix_kernel(const AsArgs a) {
+  __shared__ int s_part[kPrefixBlock];
+  __shared__ int s_off[kMaxExpertsTotal + 1];
+  __shared__ int s_cnt[kMaxExpertsTotal];
+  __shared__ int s_wtot[kPrefixBlock / kWave];
+  const int tid = threadIdx.x;
+  // G threads per expert, each over a contiguous run of waves
+  const int G = max(1, min(kPrefixBlock / a.n_exp, 8));
+  const int per = (a.n_waves + G - 1) / G;
+
+  for (int base_e = 0; base_e < a.n_exp; base_e += kPrefixBlock / G) {
+    const int e = base_e + tid / G;
+    const int g = tid % G;
+    const bool act = tid / G < kPrefixBlock / G && e < a.n_exp;
+    const int w0 = g * per, w1 = min(w0 + per, a.n_waves);
+    int sum = 0;
+    if (act)
+      for (int w = w0; w < w1; ++w) sum += a.hist[(size_t)w * a.n_exp + e];
+    s_part[tid] = sum;
+    __syncthreads();
+    if (act) {
+      int pre = 0, tot = 0;
+      for (int q = 0; q < G; ++q) {
+        const int v = s_part[(tid / G) * G + q];
+        if (q < g) pre += v;
+        tot += v;
+      }
+      if (g == 0) s_cnt[e] = tot;
+      // exclusive base of each wave within the expert (offset added later)
+      int run = pre;
+      for (int w = w0; w < w1; ++w) {
+        const int c = a.hist[(size_t)w * a.n_exp + e];
+        a.base[(size_t)w * a.n_exp + e] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+
+  layout_phase(a, s_cnt, s_off, s_wtot);
   // the per-wave bases stay relative to their expert's offset; the place
   // kernel adds the offset when it loads them
 }
+
+__device__ __forceinline__ void place_range(const AsArgs& a, int* ctr, int lo, int hi, int lane);
 
 __global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
   __shared__ int s_ctr[kAsWaves][kMaxExpertsTotal];
@@ -187,8 +206,12 @@ __global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
   for (int e = lane; e < a.n_exp; e += kWave) ctr[e] = bse[e] + a.offsets[e];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int lo = w * a.per_wave;
-  const int hi = min(lo + a.per_wave, a.n);
+  place_range(a, ctr, w * a.per_wave, min(w * a.per_wave + a.per_wave, a.n), lane);
+}
+
+// Stable placement of entries [lo, hi) by one wavefront: ctr[e] (LDS) holds
+// the next free slot of expert e in sorted order for this range.
+__device__ __forceinline__ void place_range(const AsArgs& a, int* ctr, int lo, int hi, int lane) {
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int i0 = lo; i0 < hi; i0 += kWave) {
     const int i = i0 + lane;
@@ -212,6 +235,45 @@ __global__ __launch_bounds__(kAsBlock) void as_place_kernel(const AsArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Small batches: count, merge, layout and placement in one workgroup of
+// kPrefixBlock threads (up to kFusedWaves wavefronts, each on its own
+// contiguous range), all exchanged through LDS -- one launch, no global
+// scratch.  Same results as the three-launch path.
+__global__ __launch_bounds__(kPrefixBlock) void as_fused_kernel(const AsArgs a) {
+  __shared__ int s_h[kFusedWaves][kMaxExpertsTotal];   // per-wave counts, then bases
+  __shared__ int s_off[kMaxExpertsTotal + 1];
+  __shared__ int s_cnt[kMaxExpertsTotal];
+  __shared__ int s_wtot[kPrefixBlock / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  for (int q = tid; q < kFusedWaves * a.n_exp; q += kPrefixBlock) s_h[q / a.n_exp][q % a.n_exp] = 0;
+  __syncthreads();
+  const int lo = w * a.per_wave, hi = min(lo + a.per_wave, a.n);
+  if (w < a.n_waves)
+    for (int i = lo + lane; i < hi; i += kWave) atomicAdd(&s_h[w][entry_expert(a, i)], 1);
+  __syncthreads();
+  // per expert: exclusive base of every wave's range inside the expert
+  for (int e = tid; e < a.n_exp; e += kPrefixBlock) {
+    int run = 0;
+    for (int v = 0; v < a.n_waves; ++v) {
+      const int c = s_h[v][e];
+      s_h[v][e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  layout_phase(a, s_cnt, s_off, s_wtot);
+  if (w < a.n_waves) {
+    int* ctr = s_h[w];
+    for (int e = lane; e < a.n_exp; e += kWave) ctr[e] += s_off[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    place_range(a, ctr, lo, hi, lane);
   }
 }
 
@@ -249,12 +311,20 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int
                              int32_t* sorted, int32_t* expert_ids, int32_t* offsets,
                              int32_t* npp, void* ws, hipStream_t s) {
   AsArgs a = make_args(ids, T, k, E, S, bs);
-  a.hist = reinterpret_cast<int32_t*>(ws);
-  a.base = a.hist + (size_t)a.n_waves * a.n_exp;
   a.sorted = sorted;
   a.expert_ids = expert_ids;
   a.offsets = offsets;
   a.npp = npp;
+  if (a.n <= kFusedMaxEntries) {
+    // one workgroup: at most kFusedWaves ranges of whole 64-entry chunks
+    const int chunks = std::max(1, (a.n + kWave - 1) / kWave);
+    a.per_wave = (chunks + kFusedWaves - 1) / kFusedWaves * kWave;
+    a.n_waves = std::max(1, (a.n + a.per_wave - 1) / a.per_wave);
+    hipLaunchKernelGGL(as_fused_kernel, dim3(1), dim3(kPrefixBlock), 0, s, a);
+    return hipGetLastError();
+  }
+  a.hist = reinterpret_cast<int32_t*>(ws);
+  a.base = a.hist + (size_t)a.n_waves * a.n_exp;
   const int blocks = (a.n_waves + kAsWaves - 1) / kAsWaves;
   hipLaunchKernelGGL(as_count_kernel, dim3(blocks), dim3(kAsBlock), 0, s, a);
   hipError_t err = hipGetLastError();
