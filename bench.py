@@ -439,7 +439,7 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
 
 
 def crossover_sweep(moe, W, torch, dev, stream, cfg, batches=None, kinds=(None,), steps=20,
-                    warmup=3, bs=64):
+                    warmup=3, bs=32):
     """Whole-layer time of both paths over a batch list (the configuration's
     own by default) and routing kinds (None: the configuration's own), on one
     layer's weights with several routing draws cycled."""

@@ -90,13 +90,14 @@ double expert_bytes(const moe_weights* W) {
 // Regime choice: output-centric decode for small batches, expert-centric
 // packing beyond (the warp-decode post's section on Composer).  Both costs
 // are modelled in microseconds with constants fitted to MI355X sweeps of both
-// paths over the Qwen3 (MXFP8), DeepSeek-V3 (FP8 128x128) and MXFP4 layers:
-//  decode : the touched experts' bytes at 4.5 TB/s and VALU work of
-//           1.35e-7 us per (token, slot) entry per H*I overlap, with 30% of
-//           the smaller of the two showing through, plus 8 us;
-//  grouped: the same bytes at 4.3 TB/s (3.2 TB/s for E2M1 weights, whose
+// paths (steps replayed from a HIP graph, 32-row blocks for the grouped
+// path) over the Qwen3 (MXFP8), DeepSeek-V3 (FP8 128x128) and MXFP4 layers:
+//  decode : the touched experts' bytes at 5.9 TB/s and VALU work of
+//           1.45e-7 us per (token, slot) entry per H*I overlap, with half of
+//           the smaller of the two showing through, plus 4 us;
+//  grouped: the same bytes at 5.2 TB/s (4.0 TB/s for E2M1 weights, whose
 //           stage rows are half cache lines) with the matrix work hidden,
-//           plus 45 us for sort, gather, combine and launches.
+//           plus 25 us for sort, gather, combine and launches.
 // The touched experts are their expectation under uniform routing; skewed
 // routing touches fewer, which favours the grouped path a little earlier
 // than this predicts.
@@ -106,10 +107,10 @@ int32_t model_path(const moe_weights* W, int32_t T, int32_t k) {
   const double u = n * (1.0 - std::pow(1.0 - p, (double)T)) + W->num_shared;
   const double bytes = u * expert_bytes(W);
   const double entries = (double)T * (k + W->num_shared);
-  const double valu = entries * W->hidden * W->inter * 1.35e-7;
-  const double mem_d = bytes / 4.5e6;
-  const double t_dec = std::max(mem_d, valu) + 0.3 * std::min(mem_d, valu) + 8.0;
-  const double t_grp = bytes / (W->format == MOE_W_MXFP4 ? 3.2e6 : 4.3e6) + 45.0;
+  const double valu = entries * W->hidden * W->inter * 1.45e-7;
+  const double mem_d = bytes / 5.9e6;
+  const double t_dec = std::max(mem_d, valu) + 0.5 * std::min(mem_d, valu) + 4.0;
+  const double t_grp = bytes / (W->format == MOE_W_MXFP4 ? 4.0e6 : 5.2e6) + 25.0;
   return t_grp < t_dec ? MOE_PATH_GROUPED : MOE_PATH_DECODE;
 }
 

@@ -129,18 +129,18 @@ def test_path_choice_host_logic(lib):
     assert lib.moe_choose_path(ctypes.byref(w), 16384, 8) == GRP
     # the regime follows the sweeps of both paths on MI355X where one was
     # clearly faster (whole-layer microseconds replayed from a HIP graph,
-    # decode vs grouped)
+    # decode vs grouped with 32-row blocks)
     moe = __import__("mixture_experts_decode_amd")
     qwen = _weights(moe)
-    assert lib.moe_choose_path(ctypes.byref(qwen), 16, 8) == DEC       # 79 vs 127
-    assert lib.moe_choose_path(ctypes.byref(qwen), 128, 8) == GRP      # 272 vs 176
-    assert lib.moe_choose_path(ctypes.byref(qwen), 256, 8) == GRP      # 453 vs 178
+    assert lib.moe_choose_path(ctypes.byref(qwen), 16, 8) == DEC       # 79 vs 108
+    assert lib.moe_choose_path(ctypes.byref(qwen), 128, 8) == GRP      # 273 vs 149
+    assert lib.moe_choose_path(ctypes.byref(qwen), 256, 8) == GRP      # 446 vs 153
     ds = _weights(moe, hidden=7168, inter=2048, num_experts=256, num_shared=1, format=3)
-    assert lib.moe_choose_path(ctypes.byref(ds), 1, 8) == DEC          # 77 vs 130
-    assert lib.moe_choose_path(ctypes.byref(ds), 64, 8) == GRP         # 1847 vs 1101
+    assert lib.moe_choose_path(ctypes.byref(ds), 1, 8) == DEC          # 77 vs 108
+    assert lib.moe_choose_path(ctypes.byref(ds), 64, 8) == GRP         # 1836 vs 982
     fp4 = _weights(moe, hidden=4096, inter=1536, format=2)
-    assert lib.moe_choose_path(ctypes.byref(fp4), 8, 8) == DEC         # 116 vs 204
-    assert lib.moe_choose_path(ctypes.byref(fp4), 128, 8) == GRP       # 1036 vs 412
+    assert lib.moe_choose_path(ctypes.byref(fp4), 8, 8) == DEC         # 115 vs 171
+    assert lib.moe_choose_path(ctypes.byref(fp4), 128, 8) == GRP       # 1004 vs 343
     # the choice is monotone in the batch: decode up to one crossover, then grouped
     for wt in (qwen, ds, fp4):
         picks = [lib.moe_choose_path(ctypes.byref(wt), t, 8) for t in range(0, 300)]
