@@ -29,7 +29,8 @@
 //  * 16-byte loads per lane; E4M3 / E2M1 are converted exactly to BF16 and
 //    multiplied with BF16 activations by v_dot2_f32_bf16, or converted to FP32
 //    for FP32 intermediates; the MX / tile scale multiplies each 16-byte
-//    chunk's partial sum.
+//    chunk's partial sum, except in gate_up rows converted once per item,
+//    where an MX scale (a power of two) enters the conversion itself.
 
 #include <cstdlib>
 
