@@ -44,7 +44,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--workload", default="qwen3_decode_mxfp8",
+                   help="workload name (see workloads.CONFIGS)")
     p.add_argument("--batch", type=int, default=32)
     p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
     p.add_argument("--block", type=int, default=64)
@@ -93,7 +94,7 @@ def main():
     moe.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = W.CONFIGS[args.config]
+    cfg = W.CONFIGS[args.workload]
     B = args.batch
     stream = torch.cuda.current_stream()
 
@@ -243,7 +244,7 @@ def main():
     main_res = run_steps(B, args.steps, args.warmup, args.path)
 
     sweep = []
-    if not args.no_sweep and args.config == 2:
+    if not args.no_sweep and cfg is W.QWEN3_DECODE_MXFP8:
         for b in cfg.batches:
             r = run_steps(b, 50, 5, args.path)
             sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
@@ -266,25 +267,28 @@ def main():
     del layers, arrays, w0
     torch.cuda.empty_cache()
 
-    router = [router_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t)
-              for cid, t in ((2, B), (3, 64), (4, 16384))]
+    router = [router_report(moe, W, torch, dev, stream, c, t)
+              for c, t in ((W.QWEN3_DECODE_MXFP8, B), (W.DEEPSEEK_V3_FP8_BLK128, 64),
+                           (W.PREFILL_ZIPF_MXFP8, 16384))]
 
     grouped = []
     if not args.no_grouped:
         # DeepSeek-V3-shaped layer at B = 256 (HBM-bound; 32-row blocks,
         # the fastest measured for a dozen tokens per expert) and the Zipf
         # prefill step (MFMA-bound, 128-row blocks)
-        for cid, t, bs, kind in ((3, 256, 32, None), (4, 16384, 128, "zipf")):
-            grouped.append(grouped_report(moe, W, torch, dev, stream, W.CONFIGS[cid], t, bs, kind,
+        for c, t, bs, kind in ((W.DEEPSEEK_V3_FP8_BLK128, 256, 32, None),
+                               (W.PREFILL_ZIPF_MXFP8, 16384, 128, "zipf")):
+            grouped.append(grouped_report(moe, W, torch, dev, stream, c, t, bs, kind,
                                           steps=min(args.steps, 20)))
             torch.cuda.empty_cache()
 
     crossover = []
     if args.crossover:
-        for cid, batches in ((5, None), (2, (1, 4, 8, 16, 32, 64, 128, 256)),
-                             (3, (1, 8, 16, 32, 64, 128, 224))):
-            crossover += crossover_sweep(moe, W, torch, dev, stream, W.CONFIGS[cid], batches=batches,
-                                         kinds=("uniform", "zipf") if cid == 5 else (None,))
+        for c, batches in ((W.MXFP4_SWEEP, None),
+                           (W.QWEN3_DECODE_MXFP8, (1, 4, 8, 16, 32, 64, 128, 256)),
+                           (W.DEEPSEEK_V3_FP8_BLK128, (1, 8, 16, 32, 64, 128, 224))):
+            crossover += crossover_sweep(moe, W, torch, dev, stream, c, batches=batches,
+                                         kinds=("uniform", "zipf") if c is W.MXFP4_SWEEP else (None,))
             torch.cuda.empty_cache()
 
     value = main_res["TBps"]

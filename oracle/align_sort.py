@@ -18,7 +18,7 @@ cumulative sum of the block-aligned counts, then placement):
     expert_ids[b]                   = e for every block b in [off_e/BS, off_{e+1}/BS)
     num_tokens_post_padded          = off_E
 
-Readings (listed in the design doc): the order inside an expert's run is ascending
+Readings of the pages taken here: the order inside an expert's run is ascending
 entry index (the stable order; the article's placement uses atomics and fixes
 no order, and a bit-exact comparison needs one); experts appear in ascending
 id; an expert with no entries gets no block; the sentinel is T*k; only

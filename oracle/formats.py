@@ -14,7 +14,7 @@ infinities; OCP Microscaling (MX) spec v1.0: E2M1 elements, E8M0 shared scale,
 dtype conversions, E2M1 against the OCP value table stored under
 ``tests/golden/``.
 
-Readings (listed in DESIGN.md as well):
+Readings of the pages taken here:
 * MX blocks run along the contiguous input (K) axis of each weight row.
 * FP4 packs two elements per byte, the even element in the low nibble.
 * The MX quantiser picks the shared exponent as floor(log2(amax)) minus the

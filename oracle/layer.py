@@ -10,7 +10,7 @@ each token t is routed to k experts e_tj with weights w_tj, and
     h_tj = SiLU(Wg[e_tj] x_t) * (Wu[e_tj] x_t)          (SwiGLU, SiLU(z) = z*sigmoid(z))
     y_t  = sum_j  w_tj * Wd[e_tj] h_tj                   (weighted top-k combine)
 
-Readings (each listed in the design doc):
+Readings of the pages taken here:
 * the combine uses the given weights as they are (no renormalisation);
 * the gate is the first of the two stacked projections w13[e][0], up the
   second w13[e][1]; weights are stored [out][in] with the input axis

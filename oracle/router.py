@@ -9,7 +9,7 @@ per-expert bias added for the selection in DeepSeek V3/R1 (auxiliary-loss-
 free balancing); its FasterTransformer section names the fused top-k gating
 softmax and biased top-k gating softmax operators.
 
-Readings (listed in DESIGN.md as well):
+Readings of the pages taken here:
 * selection key = score + bias, taken in float32 (the precision the kernel
   decides in); the k largest keys, ties to the lower expert index, listed in
   descending key order;

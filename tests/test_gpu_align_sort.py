@@ -34,28 +34,28 @@ def _check(lib, ids, num_experts, num_shared, bs):
 
 @pytest.mark.parametrize("bs", [16, 32, 64])
 def test_tiny_config(lib, bs):
-    cfg = W.CONFIGS[1]
+    cfg = W.TINY_FP32
     ids, _ = W.routing(cfg, 4)
     _check(lib, ids, cfg.num_experts, 0, bs)
 
 
 @pytest.mark.parametrize("bs", [64, 128])
 def test_prefill_zipf_full_size(lib, bs):
-    cfg = W.CONFIGS[4]
+    cfg = W.PREFILL_ZIPF_MXFP8
     ids, _ = W.routing(cfg, 16384)
     _check(lib, ids, cfg.num_experts, 0, bs)
 
 
 @pytest.mark.parametrize("t,bs", [(1, 32), (7, 16), (256, 64), (1000, 128)])
 def test_shared_expert_entries(lib, t, bs):
-    cfg = W.CONFIGS[3]
+    cfg = W.DEEPSEEK_V3_FP8_BLK128
     ids, _ = W.routing(cfg, t)
     _check(lib, ids, cfg.num_experts, 1, bs)
 
 
 @pytest.mark.parametrize("t", [1, 3, 64, 333, 4096])
 def test_uniform_ragged(lib, t):
-    cfg = W.CONFIGS[2]
+    cfg = W.QWEN3_DECODE_MXFP8
     ids, _ = W.routing(cfg, t)
     _check(lib, ids, cfg.num_experts, 0, 32)
 
@@ -74,7 +74,7 @@ def test_edge_cases(lib):
 
 
 def test_repeatable(lib):
-    cfg = W.CONFIGS[4]
+    cfg = W.PREFILL_ZIPF_MXFP8
     ids, _ = W.routing(cfg, 4096)
     d = torch.from_numpy(ids).cuda()
     a = lib.align_sort(d, cfg.num_experts, 0, 64)

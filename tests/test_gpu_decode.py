@@ -20,10 +20,10 @@ pytestmark = pytest.mark.gpu
 # chunks), fewer experts so the oracle stays fast; odd token counts give a
 # ragged tail of (token, slot) entries
 SMALL = {
-    "f32": W.CONFIGS[1],
-    "mxfp8": W.CONFIGS[2].replace(num_experts=16, tag=21),
-    "mxfp4": W.CONFIGS[5].replace(num_experts=16, tag=22),
-    "fp8_blk128": W.CONFIGS[3].replace(num_experts=12, tag=23),
+    "f32": W.TINY_FP32,
+    "mxfp8": W.QWEN3_DECODE_MXFP8.replace(num_experts=16, tag=21),
+    "mxfp4": W.MXFP4_SWEEP.replace(num_experts=16, tag=22),
+    "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=12, tag=23),
 }
 
 
@@ -163,19 +163,21 @@ def test_duplicate_ids_within_a_token(lib):
 
 # ---- full-size workloads, sampled tokens ---------------------------------
 
-FULL = [(2, 32, None), (2, 1, None), (3, 16, None), (5, 64, None), (5, 32, "zipf")]
+FULL = [("qwen3_decode_mxfp8", 32, None), ("qwen3_decode_mxfp8", 1, None),
+        ("deepseek_v3_fp8_blk128", 16, None), ("mxfp4_sweep", 64, None),
+        ("mxfp4_sweep", 32, "zipf")]
 
 
-@pytest.mark.parametrize("cid,t,kind", FULL)
-def test_decode_full_size_sampled(lib, cid, t, kind):
+@pytest.mark.parametrize("name,t,kind", FULL)
+def test_decode_full_size_sampled(lib, name, t, kind):
     """Full configuration and batch, in the launch shape the benchmark times;
     the oracle checks a sample of tokens (tokens are independent)."""
-    cfg = W.CONFIGS[cid]
+    cfg = W.CONFIGS[name]
     x, ids, w, h, y = _run_decode(lib, cfg, t, kind=kind)
     sample = sorted({0, t // 2, t - 1})
     x64 = L.activations_f64(x[sample], cfg.act)
     ref = L.moe_layer(x64, ids[sample], w[sample], **oracle_kw(cfg))
-    assert_layer_close(to_f64(y)[sample], ref, (cid, t))
+    assert_layer_close(to_f64(y)[sample], ref, (name, t))
 
 
 def test_out_of_range_ids_read_as_expert_zero(lib):
@@ -203,7 +205,7 @@ def test_decode_at_the_entry_limit(lib):
     """T * slots equal to moe_decode_max_entries(): the largest batch the
     decode kernels stage on chip (Qwen3-style layer, 256 tokens x top-8);
     sampled tokens against the oracle, and one past it is refused."""
-    cfg = W.CONFIGS[2]
+    cfg = W.QWEN3_DECODE_MXFP8
     limit = lib.load().moe_decode_max_entries()
     t = limit // cfg.top_k
     assert t * cfg.top_k == limit

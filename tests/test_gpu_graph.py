@@ -13,7 +13,7 @@ from _helpers import device_routing, device_weights, inputs, to_device_x
 
 pytestmark = pytest.mark.gpu
 
-CFG = W.CONFIGS[2].replace(num_experts=16, tag=41)
+CFG = W.QWEN3_DECODE_MXFP8.replace(num_experts=16, tag=41)
 
 
 def _workspace(lib, Wd, t, k, path, block):

@@ -16,9 +16,9 @@ from _helpers import (assert_layer_close, device_routing, device_weights, expert
 pytestmark = pytest.mark.gpu
 
 SMALL = {
-    "mxfp8": W.CONFIGS[4].replace(num_experts=8, tag=31),
-    "mxfp4": W.CONFIGS[5].replace(num_experts=8, tag=32),
-    "fp8_blk128": W.CONFIGS[3].replace(num_experts=6, tag=33),
+    "mxfp8": W.PREFILL_ZIPF_MXFP8.replace(num_experts=8, tag=31),
+    "mxfp4": W.MXFP4_SWEEP.replace(num_experts=8, tag=32),
+    "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=6, tag=33),
 }
 
 
@@ -200,18 +200,18 @@ def test_grouped_layer_deterministic(lib):
     assert np.array_equal(y1, y2)
 
 
-GROUPED_FULL = [(4, 16384, 128, "zipf"), (4, 16384, 64, "zipf"), (5, 256, 64, None),
-                (3, 256, 32, None)]
+GROUPED_FULL = [("prefill_zipf_mxfp8", 16384, 128, "zipf"), ("prefill_zipf_mxfp8", 16384, 64, "zipf"),
+                ("mxfp4_sweep", 256, 64, None), ("deepseek_v3_fp8_blk128", 256, 32, None)]
 
 
-@pytest.mark.parametrize("cid,t,bs,kind", GROUPED_FULL)
-def test_grouped_layer_full_size_sampled(lib, cid, t, bs, kind):
-    cfg = W.CONFIGS[cid]
+@pytest.mark.parametrize("name,t,bs,kind", GROUPED_FULL)
+def test_grouped_layer_full_size_sampled(lib, name, t, bs, kind):
+    cfg = W.CONFIGS[name]
     x, ids, w, y = _grouped_layer(lib, cfg, t, bs, kind=kind)
     sample = sorted({0, 1, t // 3, t // 2, t - 1})
     x64 = L.activations_f64(x[sample], cfg.act)
     ref = L.moe_layer(x64, ids[sample], w[sample], act_quant="mxfp8", **oracle_kw(cfg))
-    assert_layer_close(y[sample], ref, (cid, t, bs))
+    assert_layer_close(y[sample], ref, (name, t, bs))
 
 
 @pytest.mark.parametrize("t,want", [(8, "decode"), (200, "grouped")])
@@ -220,7 +220,7 @@ def test_layer_auto_matches_the_oracle_mode_of_its_path(lib, t, want):
     a small batch and expert-centric packing at a large one; each result is
     held to the oracle in the mode of the path it reports (decode: float64
     activations; grouped: MXFP8 activations and two-term h)."""
-    cfg = W.CONFIGS[2]
+    cfg = W.QWEN3_DECODE_MXFP8
     x, ids, w = inputs(cfg, t)
     Wd = device_weights(cfg)
     assert lib.choose_path(Wd, t, cfg.top_k) == want

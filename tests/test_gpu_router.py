@@ -30,16 +30,17 @@ def _check(lib, scores, k, bias=None, rows=None):
     return ids, wts
 
 
-@pytest.mark.parametrize("cid,t,kind", [(2, 32, None), (2, 1, None), (3, 64, None), (5, 256, "zipf"),
-                                        (1, 4, None)])
-def test_route_workload_scores(lib, cid, t, kind):
-    cfg = W.CONFIGS[cid]
+@pytest.mark.parametrize("name,t,kind", [("qwen3_decode_mxfp8", 32, None), ("qwen3_decode_mxfp8", 1, None),
+                                         ("deepseek_v3_fp8_blk128", 64, None), ("mxfp4_sweep", 256, "zipf"),
+                                         ("tiny_fp32", 4, None)])
+def test_route_workload_scores(lib, name, t, kind):
+    cfg = W.CONFIGS[name]
     scores, bias = W.gating_scores(cfg, t, kind)
     _check(lib, scores, cfg.top_k, bias)
 
 
 def test_route_prefill_full_size_sampled(lib):
-    cfg = W.CONFIGS[4]
+    cfg = W.PREFILL_ZIPF_MXFP8
     scores, bias = W.gating_scores(cfg, 16384)
     rows = np.unique(np.concatenate([np.arange(64), np.arange(16384 - 64, 16384),
                                      np.random.default_rng(5).integers(0, 16384, 256)]))

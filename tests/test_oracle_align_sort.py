@@ -73,10 +73,11 @@ def check_invariants(ids, e_n, bs, r):
     assert A.capacity(n, e_n, bs) >= npp
 
 
-@pytest.mark.parametrize("cid,t,bs,kind", [(1, 4, 16, None), (4, 2048, 64, "zipf"),
-                                           (4, 2048, 128, "zipf"), (2, 32, 16, None)])
-def test_matches_stable_argsort_and_invariants(cid, t, bs, kind):
-    cfg = W.CONFIGS[cid]
+@pytest.mark.parametrize("name,t,bs,kind", [("tiny_fp32", 4, 16, None), ("prefill_zipf_mxfp8", 2048, 64, "zipf"),
+                                            ("prefill_zipf_mxfp8", 2048, 128, "zipf"),
+                                            ("qwen3_decode_mxfp8", 32, 16, None)])
+def test_matches_stable_argsort_and_invariants(name, t, bs, kind):
+    cfg = W.CONFIGS[name]
     ids, _ = W.routing(cfg, t, kind=kind)
     r = A.align_sort(ids, cfg.num_experts, bs)
     s, b, off = _via_argsort(ids, cfg.num_experts, bs)

@@ -15,10 +15,10 @@ from oracle import layer as L
 from oracle import formats as F
 
 TINY = {
-    "f32": W.CONFIGS[1],
-    "mxfp8": W.CONFIGS[2].replace(hidden=64, inter=64, num_experts=4, top_k=2, tag=11),
-    "mxfp4": W.CONFIGS[5].replace(hidden=64, inter=64, num_experts=4, top_k=2, tag=12),
-    "fp8_blk128": W.CONFIGS[3].replace(hidden=256, inter=128, num_experts=4, top_k=2, num_shared=0,
+    "f32": W.TINY_FP32,
+    "mxfp8": W.QWEN3_DECODE_MXFP8.replace(hidden=64, inter=64, num_experts=4, top_k=2, tag=11),
+    "mxfp4": W.MXFP4_SWEEP.replace(hidden=64, inter=64, num_experts=4, top_k=2, tag=12),
+    "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(hidden=256, inter=128, num_experts=4, top_k=2, num_shared=0,
                                         tag=13),
 }
 

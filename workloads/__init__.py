@@ -46,7 +46,7 @@ STREAM_RANK = 6
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    cid: int
+    seed: int           # seed stream of the recipe (part of every draw's seed)
     name: str
     hidden: int
     inter: int
@@ -69,22 +69,24 @@ class Config:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = {
-    1: Config(1, "tiny_fp32", 256, 128, 8, 2, 0, "f32", "f32", "softmax_normal",
-              batches=(4,), blocks=(16,)),
-    2: Config(2, "qwen3_decode_mxfp8", 2048, 768, 128, 8, 0, "mxfp8", "bf16", "uniform",
-              batches=(1, 4, 8, 16, 32)),
-    3: Config(3, "deepseek_v3_fp8_blk128", 7168, 2048, 256, 8, 1, "fp8_blk128", "bf16",
-              "biased", batches=(1, 16, 64, 256)),
-    4: Config(4, "prefill_zipf_mxfp8", 4096, 1536, 256, 8, 0, "mxfp8", "bf16", "zipf",
-              zipf_s=1.1, batches=(16384,), blocks=(64, 128)),
-    5: Config(5, "mxfp4_sweep", 4096, 1536, 128, 8, 0, "mxfp4", "bf16", "uniform", zipf_s=1.2,
-              batches=(1, 2, 8, 32, 64, 128, 256)),
-}
+TINY_FP32 = Config(1, "tiny_fp32", 256, 128, 8, 2, 0, "f32", "f32", "softmax_normal",
+                   batches=(4,), blocks=(16,))
+QWEN3_DECODE_MXFP8 = Config(2, "qwen3_decode_mxfp8", 2048, 768, 128, 8, 0, "mxfp8", "bf16",
+                            "uniform", batches=(1, 4, 8, 16, 32))
+DEEPSEEK_V3_FP8_BLK128 = Config(3, "deepseek_v3_fp8_blk128", 7168, 2048, 256, 8, 1, "fp8_blk128",
+                                "bf16", "biased", batches=(1, 16, 64, 256))
+PREFILL_ZIPF_MXFP8 = Config(4, "prefill_zipf_mxfp8", 4096, 1536, 256, 8, 0, "mxfp8", "bf16",
+                            "zipf", zipf_s=1.1, batches=(16384,), blocks=(64, 128))
+MXFP4_SWEEP = Config(5, "mxfp4_sweep", 4096, 1536, 128, 8, 0, "mxfp4", "bf16", "uniform",
+                     zipf_s=1.2, batches=(1, 2, 8, 32, 64, 128, 256))
+
+# by workload name
+CONFIGS = {c.name: c for c in (TINY_FP32, QWEN3_DECODE_MXFP8, DEEPSEEK_V3_FP8_BLK128,
+                               PREFILL_ZIPF_MXFP8, MXFP4_SWEEP)}
 
 
 def rng(cfg, stream, *index):
-    ss = np.random.SeedSequence([cfg.cid, cfg.tag, stream] + [int(i) for i in index])
+    ss = np.random.SeedSequence([cfg.seed, cfg.tag, stream] + [int(i) for i in index])
     return np.random.Generator(np.random.PCG64(ss))
 
 
