@@ -191,7 +191,8 @@ size_t moe_align_sort_workspace_bytes(int32_t T, int32_t k, int32_t num_experts,
  *   expert_offsets    device [E+S+1] int32
  *   num_tokens_post_padded device [1] int32
  *   workspace         device, >= moe_align_sort_workspace_bytes(...)
- * block_size must be 1..1024; E+S must be 1..1024.
+ * block_size must be 1..1024; E+S must be 1..1024; k <= num_experts
+ * (MOE_ERR_INVALID_ARG otherwise).
  */
 moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k,
                           int32_t num_experts, int32_t num_shared, int32_t block_size,

@@ -82,3 +82,27 @@ def test_repeatable(lib):
     torch.cuda.synchronize()
     n = int(a["num_tokens_post_padded"].item())
     assert torch.equal(a["sorted_token_ids"][:n], b["sorted_token_ids"][:n])
+
+
+@pytest.mark.parametrize("t", [4095, 4096, 4097])
+@pytest.mark.parametrize("bs", [1, 32, 1024])
+def test_single_workgroup_limit(lib, t, bs):
+    """Up to 8192 entries one workgroup does the whole sort; one entry pair
+    past it the three-launch path runs.  Both sides of the limit, bit-exact."""
+    rng = np.random.default_rng(7 + t)
+    ids = rng.integers(0, 64, size=(t, 2)).astype(np.int32)
+    _check(lib, ids, 64, 0, bs)
+
+
+def test_random_shapes(lib):
+    """Seeded random (T, k, E, S, block) combinations across both launch
+    shapes, bit-exact against the oracle."""
+    rng = np.random.default_rng(2024)
+    for _ in range(24):
+        t = int(rng.integers(1, 3000))
+        e = int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(8, e) + 1))    # k <= E (the entry point's contract)
+        s = int(rng.integers(0, 2))
+        bs = int(rng.choice([1, 16, 32, 64, 128, 256, 1024]))
+        ids = rng.integers(0, e, size=(t, k)).astype(np.int32)
+        _check(lib, ids, e, s, bs)
