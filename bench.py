@@ -48,7 +48,7 @@ def parse():
                    help="workload name (see workloads.CONFIGS)")
     p.add_argument("--batch", type=int, default=32)
     p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
-    p.add_argument("--block", type=int, default=64)
+    p.add_argument("--block", type=int, default=0)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-copy-peak", action="store_true")

@@ -313,7 +313,10 @@ size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k,
 /*
  * moe_layer: y = the routed-expert FFN of the layer for T tokens.
  *   path        MOE_PATH_AUTO / DECODE / GROUPED
- *   block_size  grouped path M block (32, 64 or 128); ignored for decode
+ *   block_size  grouped path M block (32, 64 or 128), or 0: the library picks
+ *               by the expected entries per expert (32 up to 48, 64 up to
+ *               160, else 128; the same rule in moe_layer_workspace_bytes);
+ *               ignored for decode
  *   chosen      host, nullable: receives the path that ran
  *   workspace   device, >= moe_layer_workspace_bytes(W, T, k, path, block_size)
  * The decode path keeps activations exact (BF16/FP32 in, FP32 accumulate);

@@ -280,12 +280,12 @@ def choose_path(W, t, k):
     return PATH_NAME[_lib.moe_choose_path(W.ref, t, k)]
 
 
-def layer_workspace_bytes(W, t, k, path="auto", block=64):
+def layer_workspace_bytes(W, t, k, path="auto", block=0):
     load()
     return _lib.moe_layer_workspace_bytes(W.ref, t, k, PATH[path], block)
 
 
-def layer(W, x, topk_ids, topk_weights, path="auto", block=64, y=None, y_dtype="f32",
+def layer(W, x, topk_ids, topk_weights, path="auto", block=0, y=None, y_dtype="f32",
           workspace=None, stream=None):
     """y [T][H] for the whole layer; returns (y, path that ran)."""
     load()

@@ -76,6 +76,15 @@ bool grouped_supported(const moe_weights* W) {
 
 bool block_ok(int32_t bs) { return bs == 32 || bs == 64 || bs == 128; }
 
+// Grouped M block for block_size == 0: by the expected (token, slot) entries
+// per expert under uniform routing.  32-row blocks were fastest measured at
+// decode-like loads (about 9-16 entries per expert), 128 at the 16384-token
+// prefill (about 512).
+int32_t auto_block(const moe_weights* W, int32_t T, int32_t k) {
+  const double per = (double)T * (k + W->num_shared) / (W->num_experts + W->num_shared);
+  return per <= 48.0 ? 32 : per <= 160.0 ? 64 : 128;
+}
+
 // Stored bytes of one expert (weights and scales of gate, up and down).
 double expert_bytes(const moe_weights* W) {
   const double hi = (double)W->hidden * W->inter;
@@ -341,6 +350,7 @@ size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k, int
   if (check_weights(W) != MOE_OK || T < 0 || k < 0) return 0;
   if (path == MOE_PATH_AUTO) path = moe_choose_path(W, T, k);
   if (path == MOE_PATH_DECODE) return decode_workspace(W, T, k);
+  if (block_size == 0) block_size = auto_block(W, T, k);
   if (path == MOE_PATH_GROUPED && block_ok(block_size))
     return grouped_layout(W, T, k, block_size).total;
   return 0;
@@ -377,6 +387,7 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
                     stream);
   }
   // grouped
+  if (block_size == 0) block_size = auto_block(W, T, k);
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
   if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
   const GroupedLayout L = grouped_layout(W, T, k, block_size);

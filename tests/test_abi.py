@@ -153,3 +153,8 @@ def test_path_choice_host_logic(lib):
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * (768 * 2 + 2048 * 4)
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 64) > 0
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 48) == 0
+    # block 0: the library picks by expected entries per expert (32 at 2 per
+    # expert, 64 at 64, 128 at 1024)
+    for t, bs in ((32, 32), (1024, 64), (16384, 128)):
+        assert (lib.moe_layer_workspace_bytes(ctypes.byref(w), t, 8, GRP, 0) ==
+                lib.moe_layer_workspace_bytes(ctypes.byref(w), t, 8, GRP, bs))
