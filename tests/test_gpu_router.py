@@ -75,3 +75,30 @@ def test_route_ties_and_signed_zero(lib):
 def test_route_empty_batch(lib):
     ids, wts = _route(lib, np.zeros((0, 32), dtype=np.float32), 4)
     assert ids.shape == (0, 4) and wts.shape == (0, 4)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_router_feeds_the_layer(lib, path):
+    """Scores -> moe_topk_route -> moe_layer on the device, against the
+    oracle router feeding the oracle layer (DeepSeek-style selection bias,
+    shared expert).  The routed ids match bit for bit, so the layer is held
+    to the usual parity bound of the path that ran."""
+    from _helpers import assert_layer_close, device_weights, oracle_kw, to_device_x, to_f64
+    from oracle import layer as L
+    cfg = W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=16, hidden=1024, inter=512, tag=51)
+    t = 24
+    scores, bias = W.gating_scores(cfg, t)
+    s = torch.from_numpy(scores).cuda()
+    b = torch.from_numpy(bias).cuda()
+    ids, wts = lib.topk_route(s, cfg.top_k, bias=b)
+    x = W.activations(cfg, t)
+    Wd = device_weights(cfg)
+    y, chosen = lib.layer(Wd, to_device_x(cfg, x), ids, wts, path=path)
+    torch.cuda.synchronize()
+    assert chosen == path
+    ref_ids, ref_w = R.topk_route(scores, cfg.top_k, bias)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    mode = "none" if path == "decode" else "mxfp8"
+    ref = L.moe_layer(L.activations_f64(x, cfg.act), ref_ids.astype(np.int32),
+                      ref_w.astype(np.float32), act_quant=mode, **oracle_kw(cfg))
+    assert_layer_close(to_f64(y), ref, path)
