@@ -378,7 +378,7 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
     k, S = cfg.top_k, cfg.num_shared
     slots = k + S
     y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
-    slot_out = torch.empty((t * slots, cfg.hidden), dtype=torch.float32, device=dev)
+    slot_out = torch.empty((t * slots, cfg.hidden), dtype=torch.bfloat16, device=dev)
     cap = moe.align_sort_capacity(t, k, cfg.num_experts, S, bs)
 
     def step(ev=None):

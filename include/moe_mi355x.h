@@ -248,23 +248,25 @@ moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const ui
  * hq/hs laid out as moe_grouped_gate_up writes them; row r of O is multiplied
  * by the routing weight of entry
  * i = sorted_token_ids[r] (1.0 for the shared slot) and stored to
- * slot_out[i][:]; sentinel rows are dropped (warp-decode post, buffer
- * section: the per-expert output buffer of the expert-centric path).
- *   slot_out device [T*slots][H] float32
+ * slot_out[i][:], rounded once to BF16 (round to nearest even); sentinel rows
+ * are dropped (warp-decode post, buffer section: the per-expert output buffer
+ * of the expert-centric path, 2-byte values).
+ *   slot_out device [T*slots][H] BF16 bit patterns
  */
 moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8_t* hs,
                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
                             const int32_t* num_tokens_post_padded, int32_t capacity,
                             int32_t block_size, const float* topk_weights, int32_t T,
-                            int32_t k, float* slot_out, void* stream);
+                            int32_t k, uint16_t* slot_out, void* stream);
 
 /*
  * moe_combine: y[t][d] = sum_{j < slots} slot_out[t*slots + j][d], summed in
- * slot order (deterministic; warp-decode post, traditional path: the final
- * combine of per-expert outputs).
+ * slot order in FP32 (deterministic; warp-decode post, traditional path: the
+ * final combine of per-expert outputs).
+ *   slot_out device [T*slots][H] BF16 bit patterns (as moe_grouped_down writes)
  *   y device [T][H], y_dtype
  */
-moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t H,
+moe_status moe_combine(const uint16_t* slot_out, int32_t T, int32_t slots, int32_t H,
                        void* y, int32_t y_dtype, void* stream);
 
 /* ------------------------------------------------------------------ */

@@ -240,8 +240,10 @@ def grouped_down(W, hq, hs, sorted_ids, expert_ids, npp, capacity, block, topk_w
                  slot_out=None, stream=None):
     load()
     if slot_out is None:
-        slot_out = torch.empty((t * (k + W.num_shared), W.hidden), dtype=torch.float32,
+        slot_out = torch.empty((t * (k + W.num_shared), W.hidden), dtype=torch.bfloat16,
                                device=hq.device)
+    if slot_out.dtype != torch.bfloat16:
+        raise TypeError("slot_out holds BF16 values")
     st = _lib.moe_grouped_down(W.ref, _ptr(hq), _ptr(hs), _ptr(sorted_ids), _ptr(expert_ids),
                                _ptr(npp), capacity, block, _ptr(topk_weights), t, k,
                                _ptr(slot_out), _stream(stream))
@@ -251,6 +253,8 @@ def grouped_down(W, hq, hs, sorted_ids, expert_ids, npp, capacity, block, topk_w
 
 def combine(slot_out, t, slots, y=None, y_dtype="f32", stream=None):
     load()
+    if slot_out.dtype != torch.bfloat16:
+        raise TypeError("slot_out holds BF16 values (as grouped_down writes them)")
     h = slot_out.shape[1]
     if y is None:
         y = _alloc((t, h), y_dtype, slot_out.device)

@@ -145,7 +145,7 @@ GroupedLayout grouped_layout(const moe_weights* W, int32_t T, int32_t k, int32_t
   L.xs = take((size_t)L.cap * (W->hidden / 32));
   L.hq = take((size_t)2 * L.cap * W->inter);          // hi and lo terms
   L.hs = take((size_t)2 * L.cap * (W->inter / 32));
-  L.slot_out = take((size_t)n * W->hidden * 4);
+  L.slot_out = take((size_t)n * W->hidden * 2);      // BF16 slot outputs
   L.total = off;
   return L;
 }
@@ -301,7 +301,7 @@ moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8
                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
                             const int32_t* num_tokens_post_padded, int32_t capacity,
                             int32_t block_size, const float* topk_weights, int32_t T, int32_t k,
-                            float* slot_out, void* stream) {
+                            uint16_t* slot_out, void* stream) {
   moe_status st = check_weights(W);
   if (st != MOE_OK) return st;
   if ((st = check_routing(W, T, k)) != MOE_OK) return st;
@@ -317,12 +317,13 @@ moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8
                                            topk_weights, T, k, slot_out, as_stream(stream)));
 }
 
-moe_status moe_combine(const float* slot_out, int32_t T, int32_t slots, int32_t H, void* y,
+moe_status moe_combine(const uint16_t* slot_out, int32_t T, int32_t slots, int32_t H, void* y,
                        int32_t y_dtype, void* stream) {
   if (T < 0 || slots < 1 || H <= 0 || !dtype_ok(y_dtype)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!slot_out || !y) return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_combine(slot_out, T, slots, H, y, y_dtype, as_stream(stream)));
+  return from_hip(moe::launch_combine(slot_out, MOE_DT_BF16, T, slots, H, y, y_dtype,
+                                      as_stream(stream)));
 }
 
 moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int32_t E, int32_t k,
@@ -402,7 +403,7 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + L.hs);
-  float* so = reinterpret_cast<float*>(ws + L.slot_out);
+  uint16_t* so = reinterpret_cast<uint16_t*>(ws + L.slot_out);
   hipError_t e = moe::launch_align_sort(topk_ids, T, k, W->num_experts, W->num_shared, block_size,
                                         sorted, eids, offs, npp, ws + L.as_ws, s);
   if (e != hipSuccess) return from_hip(e);
@@ -413,7 +414,7 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   e = moe::launch_grouped_down(*W, hq, hs, sorted, eids, npp, L.cap, block_size, topk_weights, T,
                                k, so, s);
   if (e != hipSuccess) return from_hip(e);
-  return from_hip(moe::launch_combine(so, T, slots, W->hidden, y, y_dtype, s));
+  return from_hip(moe::launch_combine(so, MOE_DT_BF16, T, slots, W->hidden, y, y_dtype, s));
 }
 
 // ---- measurement helpers -----------------------------------------------

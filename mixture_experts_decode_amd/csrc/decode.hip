@@ -820,7 +820,7 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
       return hipErrorInvalidValue;
   }
   if (err != hipSuccess || !em) return err;
-  return launch_combine(slot_out, T, a.slots, W.hidden, y, y_dtype, s);
+  return launch_combine(slot_out, MOE_DT_F32, T, a.slots, W.hidden, y, y_dtype, s);
 }
 
 }  // namespace moe

@@ -109,8 +109,10 @@ __global__ __launch_bounds__(kGqBlock) void gather_quant_kernel(
   }
 }
 
-template <bool YBF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ so, int T,
+// Slots are FP32 (decode path) or BF16 (grouped path); the sum is FP32 in
+// slot order either way.
+template <bool YBF16, bool SBF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ so, int T,
                                                       int slots, int H, void* __restrict__ y) {
   const int h4 = H >> 2;
   const size_t n = (size_t)T * h4;
@@ -119,7 +121,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const size_t c = i - t * h4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < slots; ++j) {
-      const float4 v = reinterpret_cast<const float4*>(so + ((t * slots + j) * H))[c];
+      float4 v;
+      if constexpr (SBF16) {
+        const uint2 q =
+            reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(so) + (t * slots + j) * H)[c];
+        v = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+      } else {
+        v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(so) + (t * slots + j) * H)[c];
+      }
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -153,15 +162,21 @@ hipError_t launch_gather_quant(const void* x, int x_dtype, int T, int H, int slo
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* y, int y_dtype,
-                          hipStream_t s) {
+hipError_t launch_combine(const void* slot_out, int slot_dtype, int T, int slots, int H, void* y,
+                          int y_dtype, hipStream_t s) {
   if (H % 4) return hipErrorNotSupported;
   const size_t n = (size_t)T * (H / 4);
+  if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((n + 255) / 256, (size_t)device_num_cus() * 16);
-  if (y_dtype == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
+  const bool yb = y_dtype == MOE_DT_BF16, sb = slot_dtype == MOE_DT_BF16;
+  if (yb && sb)
+    hipLaunchKernelGGL((combine_kernel<true, true>), dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
+  else if (yb)
+    hipLaunchKernelGGL((combine_kernel<true, false>), dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
+  else if (sb)
+    hipLaunchKernelGGL((combine_kernel<false, true>), dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
+    hipLaunchKernelGGL((combine_kernel<false, false>), dim3(blocks), dim3(256), 0, s, slot_out, T, slots, H, y);
   return hipGetLastError();
 }
 
@@ -208,7 +223,7 @@ struct GemmArgs {
   uint8_t* hq;             // gate_up out [2][cap][I]: hi term, then lo term
   uint8_t* hs;             // gate_up out [2][cap][I/32]
   int cap;
-  float* out;              // down out: slot_out [T*slots][H]
+  uint16_t* out;           // down out: slot_out [T*slots][H] BF16
   int K, N;                // reduction length, output columns (neurons or H)
   int I, H;
   int b_row_bytes;
@@ -667,19 +682,19 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
 #pragma unroll
       for (int m = 0; m < MF; ++m) {
         if (ent[m] < 0 || ent[m] >= g.sentinel) continue;
-        float* out = g.out + (size_t)ent[m] * g.H;
+        uint16_t* out = g.out + (size_t)ent[m] * g.H;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int c0 = tile_nt * BN + wn * S::WCOLS + 32 * f + 4 * h;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (c0 + 8 * r < g.N) {
-              float4 v;
-              v.x = __fmul_rn(acc[m][f][4 * r + 0], wgt[m]);
-              v.y = __fmul_rn(acc[m][f][4 * r + 1], wgt[m]);
-              v.z = __fmul_rn(acc[m][f][4 * r + 2], wgt[m]);
-              v.w = __fmul_rn(acc[m][f][4 * r + 3], wgt[m]);
-              *reinterpret_cast<float4*>(out + c0 + 8 * r) = v;
+              // w * row, rounded once to BF16 (the slot buffer's format)
+              const uint32_t b0 = f32_to_bf16_bits(__fmul_rn(acc[m][f][4 * r + 0], wgt[m]));
+              const uint32_t b1 = f32_to_bf16_bits(__fmul_rn(acc[m][f][4 * r + 1], wgt[m]));
+              const uint32_t b2 = f32_to_bf16_bits(__fmul_rn(acc[m][f][4 * r + 2], wgt[m]));
+              const uint32_t b3 = f32_to_bf16_bits(__fmul_rn(acc[m][f][4 * r + 3], wgt[m]));
+              *reinterpret_cast<uint2*>(out + c0 + 8 * r) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
             }
           }
         }
@@ -765,7 +780,7 @@ hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const
 hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const uint8_t* hs,
                                const int32_t* sorted, const int32_t* expert_ids,
                                const int32_t* npp, int capacity, int bs, const float* wts, int T,
-                               int k, float* slot_out, hipStream_t s) {
+                               int k, uint16_t* slot_out, hipStream_t s) {
   if (capacity / bs == 0) return hipSuccess;
   GemmArgs a{};
   a.a = hq;

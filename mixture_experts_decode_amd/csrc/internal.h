@@ -47,11 +47,12 @@ hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const
 hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const uint8_t* hs,
                                const int32_t* sorted, const int32_t* expert_ids,
                                const int32_t* npp, int capacity, int bs, const float* wts,
-                               int T, int k, float* slot_out, hipStream_t s);
+                               int T, int k, uint16_t* slot_out, hipStream_t s);
 hipError_t launch_topk_route(const float* scores, const float* bias, int T, int E, int k,
                              int32_t* ids, float* wts, hipStream_t s);
-hipError_t launch_combine(const float* slot_out, int T, int slots, int H, void* y, int y_dtype,
-                          hipStream_t s);
+// slot_dtype MOE_DT_F32 (decode path) or MOE_DT_BF16 (grouped path)
+hipError_t launch_combine(const void* slot_out, int slot_dtype, int T, int slots, int H, void* y,
+                          int y_dtype, hipStream_t s);
 
 // util.hip
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

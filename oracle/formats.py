@@ -78,6 +78,17 @@ def decode_bf16(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(v):
+    """float64 -> the nearest BF16 value (round to nearest, ties to even on the
+    8-bit significand), as float64.  Finite inputs within the float32 range;
+    BF16 keeps float32's exponent range, so only the significand is rounded
+    (below 2^-126 the spacing stays 2^-133, the subnormal step)."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                        # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)               # spacing of 8 significant bits
+    return np.ldexp(np.round(np.ldexp(v, -q)), q)
+
+
 def unpack_fp4(packed):
     """[..., n/2] bytes -> [..., n] E2M1 codes; element 2p is the low nibble of
     byte p and element 2p+1 its high nibble."""

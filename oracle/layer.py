@@ -27,7 +27,11 @@ Readings of the pages taken here:
   SwiGLU with requantisation) as two MXFP8 terms, hi = Q(h) and lo = Q(h - hi),
   both fed to the down product.  A single term would let the matrix core's own
   accumulation error (about 5e-5 relative on gfx950) flip requantised codes
-  against any exact reference; the second term absorbs such flips.  With
+  against any exact reference; the second term absorbs such flips.  The
+  expert-centric path also keeps each slot's weighted output w_tj * Wd h_tj in
+  a BF16 buffer before the combine (the warp-decode post sizes that buffer
+  with 2-byte values: top-k x hidden x 2 bytes per token), so in this mode
+  every slot contribution is rounded to BF16 before the slot-order sum.  With
   ``act_quant="none"`` activations stay exact, as on the output-centric path.
 
 All arithmetic is float64.  Experts are dequantised once per call, each only
@@ -149,7 +153,8 @@ def gate_up(x, topk_ids, *, fmt, num_experts, num_shared, get_expert, act_quant=
 
 def down(h, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert, act_quant="none"):
     """y [T][H] float64 from a given h [T][k+S][I]: y_t = sum_j w_tj Wd h_tj,
-    summed over j in slot order."""
+    summed over j in slot order (mode mxfp8: h as two MXFP8 terms and every
+    slot contribution rounded to BF16, as in moe_layer)."""
     ids, w = slots(topk_ids, topk_weights, num_experts, num_shared)
     hh = (F.fake_quant_mx_e4m3_two_term(h) if act_quant == "mxfp8"
           else np.asarray(h, dtype=np.float64))
@@ -158,7 +163,8 @@ def down(h, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert,
         _, _, wd = dequant_expert(fmt, get_expert(e))
         if ys is None:
             ys = np.zeros(ids.shape + (wd.shape[0],))
-        ys[rows, cols] = (hh[rows, cols] @ wd.T) * w[rows, cols][:, None]
+        contrib = (hh[rows, cols] @ wd.T) * w[rows, cols][:, None]
+        ys[rows, cols] = F.round_to_bf16(contrib) if act_quant == "mxfp8" else contrib
     y = np.zeros((ids.shape[0], ys.shape[2]))
     for j in range(ids.shape[1]):
         y += ys[:, j]
@@ -181,7 +187,8 @@ def moe_layer(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_ex
             hh = F.fake_quant_mx_e4m3_two_term(hh)
         if ys is None:
             ys = np.zeros(ids.shape + (wd.shape[0],))
-        ys[rows, cols] = (hh @ wd.T) * w[rows, cols][:, None]
+        contrib = (hh @ wd.T) * w[rows, cols][:, None]
+        ys[rows, cols] = F.round_to_bf16(contrib) if act_quant == "mxfp8" else contrib
     y = np.zeros((ids.shape[0], ys.shape[2]))
     for j in range(ids.shape[1]):
         y += ys[:, j]
@@ -218,7 +225,10 @@ def moe_layer_scalar(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared,
                 h.append(g / (1.0 + math.exp(-g)) * u)
             if act_quant == "mxfp8":
                 h = [float(v) for v in F.fake_quant_mx_e4m3_two_term(np.array(h))]
-            contrib.append([w[t, j] * math.fsum(wd[d, n] * h[n] for n in range(n_i))
-                            for d in range(wd.shape[0])])
+            c = [w[t, j] * math.fsum(wd[d, n] * h[n] for n in range(n_i))
+                 for d in range(wd.shape[0])]
+            if act_quant == "mxfp8":
+                c = [float(v) for v in F.round_to_bf16(np.array(c))]
+            contrib.append(c)
         rows.append([math.fsum(c[d] for c in contrib) for d in range(len(contrib[0]))])
     return np.array(rows, dtype=np.float64)

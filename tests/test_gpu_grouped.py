@@ -117,7 +117,7 @@ def test_grouped_gate_up_alone(lib, fmt, bs):
                                     ("mxfp8", 32), ("mxfp4", 64),
                                     ("fp8_blk128", 128)])
 def test_grouped_down_alone(lib, fmt, bs):
-    """a8 on generator-made two-term MXFP8 h: slot_out[i] = w_i * Wd (hi + lo)
+    """a8 on generator-made two-term MXFP8 h: slot_out[i] = BF16(w_i * Wd (hi + lo))
     for every real (non-padding) sorted row; padding rows write nothing."""
     cfg = SMALL[fmt].replace(num_shared=0, top_k=2)
     t = 70
@@ -129,7 +129,7 @@ def test_grouped_down_alone(lib, fmt, bs):
     hq_np, hs_np = np.stack([hi_q, lo_q]), np.stack([hi_s, lo_s])
     Wd = device_weights(cfg)
     idd, wd = device_routing(ids, w)
-    so = torch.full((t * cfg.top_k, cfg.hidden), float("nan"), device="cuda")
+    so = torch.full((t * cfg.top_k, cfg.hidden), float("nan"), device="cuda", dtype=torch.bfloat16)
     lib.grouped_down(Wd, torch.from_numpy(hq_np).cuda(), torch.from_numpy(hs_np).cuda(),
                      sort["sorted_token_ids"], sort["expert_ids"], sort["num_tokens_post_padded"],
                      cap, bs, wd, t, cfg.top_k, slot_out=so)
@@ -144,20 +144,26 @@ def test_grouped_down_alone(lib, fmt, bs):
             ent = ref["sorted_token_ids"][r]
             if ent < t * cfg.top_k:
                 want[ent] = (wdn @ h[r]) * float(w.reshape(-1)[ent])
-    got = so.cpu().numpy().astype(np.float64)
+    got = to_f64(so)
     assert np.isfinite(got).all()           # every slot row written exactly by its sorted row
     # exact products (E4M3 x E4M3/E2M1 with power-of-two scales), FP32
-    # accumulation over I terms inside the matrix core: ~1e-5 relative
+    # accumulation over I terms inside the matrix core (~1e-5 relative), then
+    # one BF16 rounding on each side: almost every value is the oracle's BF16
+    # value itself, the rest are one BF16 step away
+    want = F.round_to_bf16(want)
+    same = np.mean(got == want)
+    assert same > 0.98, same
     m = metrics(got, want)
-    assert m["min_cos"] > 0.999999 and m["max_rel_l2"] < 1e-4, m
+    assert m["min_cos"] > 0.999999 and m["max_rel_l2"] < 1e-3, m
 
 
 def test_combine_slot_order(lib):
     t, slots, h = 37, 9, 2048
     rng = np.random.default_rng(11)
-    so = rng.standard_normal((t * slots, h)).astype(np.float32)
-    y = lib.combine(torch.from_numpy(so).cuda(), t, slots)
-    yb = lib.combine(torch.from_numpy(so).cuda(), t, slots, y_dtype="bf16")
+    sob = torch.from_numpy(rng.standard_normal((t * slots, h)).astype(np.float32)).to(torch.bfloat16)
+    so = sob.to(torch.float32).numpy()      # the BF16 slot values, exactly
+    y = lib.combine(sob.cuda(), t, slots)
+    yb = lib.combine(sob.cuda(), t, slots, y_dtype="bf16")
     torch.cuda.synchronize()
     want = np.zeros((t, h), dtype=np.float32)
     for j in range(slots):                   # float32 sums in slot order

@@ -160,3 +160,20 @@ def test_two_term_mx_quantisation():
     lo2 = F.fake_quant_mx_e4m3(v - hi2)
     assert np.abs((hi2 + lo2) - v)[0, :32].max() <= np.abs(v[0, :32]).max() * 2.0 ** -6
     assert np.abs(hi - v).max() > np.abs(approx - v).max()
+
+
+def test_round_to_bf16_vs_torch_and_ties():
+    """float32 inputs: equal to torch's float32 -> bfloat16 cast (RNE);
+    exact halfway cases go to the even significand; idempotent."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000) * 1e-39]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = F.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: even significand is 1.0;
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6
+    assert F.round_to_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert F.round_to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert F.round_to_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -40)) == -(1.0 + 2.0 ** -7)
+    assert np.array_equal(F.round_to_bf16(got), got)

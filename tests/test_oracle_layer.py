@@ -171,14 +171,22 @@ def test_gate_up_then_down_is_the_layer():
 
 def test_mxfp8_mode_quantises_activations():
     """Mode mxfp8 equals mode none run on Q(x) with h replaced by its two-term
-    MXFP8 form Q(h) + Q(h - Q(h))."""
+    MXFP8 form Q(h) + Q(h - Q(h)) and every slot's weighted output rounded to
+    BF16 before the slot-order sum (each slot taken alone through mode none
+    by zeroing the other slots' weights)."""
     cfg = TINY["mxfp8"]
+    assert cfg.num_shared == 0
     x, ids, w = _inputs(cfg, 3)
     kw = _kw(cfg)
     xq = F.fake_quant_mx_e4m3(x)
     h = L.gate_up(xq, ids, **kw)
     hq = F.fake_quant_mx_e4m3(h)
-    y_ref = L.down(hq + F.fake_quant_mx_e4m3(h - hq), ids, w, **kw)
+    hh = hq + F.fake_quant_mx_e4m3(h - hq)
+    y_ref = np.zeros((x.shape[0], cfg.hidden))
+    for j in range(ids.shape[1]):
+        wj = np.zeros_like(w)
+        wj[:, j] = w[:, j]
+        y_ref = y_ref + F.round_to_bf16(L.down(hh, ids, wj, **kw))
     assert np.allclose(L.moe_layer(x, ids, w, act_quant="mxfp8", **kw), y_ref, rtol=0, atol=1e-13)
     # and it differs from mode none (the quantisation is really applied)
     assert not np.allclose(L.moe_layer(x, ids, w, **kw), y_ref, rtol=0, atol=1e-6)
