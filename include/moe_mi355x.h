@@ -322,7 +322,8 @@ size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k,
  *   chosen      host, nullable: receives the path that ran
  *   workspace   device, >= moe_layer_workspace_bytes(W, T, k, path, block_size)
  * The decode path keeps activations exact (BF16/FP32 in, FP32 accumulate);
- * the grouped path quantises x and h to MXFP8 for the matrix cores.
+ * the grouped path quantises x and h to MXFP8 for the matrix cores and holds
+ * each slot's weighted output in BF16 before the combine.
  */
 moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
                      const int32_t* topk_ids, const float* topk_weights,
