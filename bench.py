@@ -305,7 +305,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-weights/bf16-act/f32-acc" if cfg.fmt == "mxfp8" else cfg.fmt,
+        # the multiply-accumulate type of the timed path: BF16 operands (the
+        # stored E4M3/E2M1 weights convert to BF16 exactly) with FP32 sums
+        "dtype": "f32" if cfg.fmt == "f32" else "bf16",
+        "precision": f"{cfg.fmt} weights, {cfg.act} activations, f32 accumulation",
         "data": "synthetic (seeded; random-init weights of the named shape)",
         "config": {"workload": cfg.name, "hidden": cfg.hidden, "inter": cfg.inter,
                    "experts": cfg.num_experts, "top_k": cfg.top_k, "batch": B,
