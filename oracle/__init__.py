@@ -17,7 +17,11 @@ What is computed, and where it comes from:
   MXFP8 weights converted to FP32 on the fly; GC-MoE abstract: FP8/FP4).
 * ``layer``     -- the MoE layer itself: y_t = sum_j w_tj * Wd_e (SiLU(Wg_e x_t) *
   Wu_e x_t), in float64, from identically dequantised weights (warp-decode post,
-  sections on the traditional MoE path and on how the two kernels work).
+  sections on the traditional MoE path and on how the two kernels work), with
+  exact activations (mode ``none``, the output-centric path) or with the
+  expert-centric path's MX activations and BF16 slot outputs, h requantised
+  with two terms (mode ``mxfp8``, what the grouped path computes) or one
+  (mode ``mxfp8_single``, the plain reading of the pages).
 * ``align_sort``-- the block-padded, expert-grouped ordering of (token, slot)
   entries (align-and-sort article, background section and the D-C-P section).
 * ``router``    -- the router front-end: gating scores (+ bias) -> top-k ids and

@@ -19,20 +19,26 @@ Readings of the pages taken here:
   slot k with weight 1.0 for every token (the align-and-sort article notes
   DeepSeek's single shared expert; its weight is not stated, 1.0 is the plain
   reading);
-* ``act_quant="mxfp8"`` models the expert-centric path, whose block-scaled
-  matrix cores need 8-bit operands: x_t is MX-quantised per 32 along H before
-  the gate/up products (the align-and-sort article's online FP8 quantisation
-  step in the fused pipeline; the warp-decode post, accuracy section, on this
-  extra rounding), and h_tj is requantised per 32 along I (GC-MoE abstract:
-  SwiGLU with requantisation) as two MXFP8 terms, hi = Q(h) and lo = Q(h - hi),
-  both fed to the down product.  A single term would let the matrix core's own
-  accumulation error (about 5e-5 relative on gfx950) flip requantised codes
-  against any exact reference; the second term absorbs such flips.  The
-  expert-centric path also keeps each slot's weighted output w_tj * Wd h_tj in
-  a BF16 buffer before the combine (the warp-decode post sizes that buffer
-  with 2-byte values: top-k x hidden x 2 bytes per token), so in this mode
-  every slot contribution is rounded to BF16 before the slot-order sum.  With
-  ``act_quant="none"`` activations stay exact, as on the output-centric path.
+* the expert-centric path runs its products on block-scaled matrix cores,
+  which take 8-bit operands, so its activations are MX-quantised: x_t per 32
+  along H before the gate/up products (the align-and-sort article's online
+  FP8 quantisation step in the fused pipeline; the warp-decode post, accuracy
+  section, on this extra rounding), and h_tj per 32 along I after SwiGLU
+  (GC-MoE abstract: SwiGLU fused with requantisation).  It also keeps each
+  slot's weighted output w_tj * Wd h_tj in a 2-byte buffer before the combine
+  (the warp-decode post sizes that buffer as top-k x hidden x 2 bytes per
+  token), read here as BF16 with round-to-nearest-even, so every slot
+  contribution is rounded to BF16 before the slot-order sum.  No page says
+  how many terms the requantisation of h keeps.  Two modes:
+    - ``act_quant="mxfp8_single"``: h -> Q(h), one MXFP8 term: the plain
+      reading of "requantization";
+    - ``act_quant="mxfp8"``: h -> Q(h) + Q(h - Q(h)), two MXFP8 terms, both
+      fed to the down product.  This is the library's own design choice: a
+      matrix core's accumulation error moves h by about 5e-5 relative, which
+      flips some single-term codes against any exact reference; the second
+      term absorbs such flips.  The library's grouped path computes this mode.
+  With ``act_quant="none"`` activations stay exact, as on the output-centric
+  path.
 
 All arithmetic is float64.  Experts are dequantised once per call, each only
 if some slot routes to it.
@@ -116,6 +122,33 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+MODES = ("none", "mxfp8", "mxfp8_single")
+
+
+def _check_mode(act_quant):
+    if act_quant not in MODES:
+        raise ValueError(act_quant)
+
+
+def quantise_x(x, act_quant):
+    """The gate/up products' input: x itself, or its MX form Q(x)."""
+    return x if act_quant == "none" else F.fake_quant_mx_e4m3(x)
+
+
+def quantise_h(h, act_quant):
+    """The down product's input: h itself, Q(h), or Q(h) + Q(h - Q(h))."""
+    if act_quant == "mxfp8":
+        return F.fake_quant_mx_e4m3_two_term(h)
+    if act_quant == "mxfp8_single":
+        return F.fake_quant_mx_e4m3(h)
+    return np.asarray(h, dtype=np.float64)
+
+
+def round_slot(c, act_quant):
+    """A slot's weighted output as the path holds it before the combine."""
+    return c if act_quant == "none" else F.round_to_bf16(c)
+
+
 # --------------------------------------------------------------------------
 # the layer, vectorised by grouping slots per expert
 # --------------------------------------------------------------------------
@@ -135,12 +168,13 @@ def _group(ids):
 def gate_up(x, topk_ids, *, fmt, num_experts, num_shared, get_expert, act_quant="none"):
     """h [T][k+S][I] float64: h_tj = SiLU(Wg x_t) * (Wu x_t) for e = e_tj.
 
-    x: float64 [T][H].  With act_quant="mxfp8" the rows of x are MX-quantised
+    x: float64 [T][H].  In the MXFP8 modes the rows of x are MX-quantised
     first and h is returned unquantised (the quantisation of h belongs to the
     down product).
     """
+    _check_mode(act_quant)
     ids, _ = slots(topk_ids, None, num_experts, num_shared)
-    a = F.fake_quant_mx_e4m3(x) if act_quant == "mxfp8" else x
+    a = quantise_x(x, act_quant)
     h = None
     for e, rows, cols in _group(ids):
         wg, wu, _ = dequant_expert(fmt, get_expert(e))
@@ -153,18 +187,18 @@ def gate_up(x, topk_ids, *, fmt, num_experts, num_shared, get_expert, act_quant=
 
 def down(h, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert, act_quant="none"):
     """y [T][H] float64 from a given h [T][k+S][I]: y_t = sum_j w_tj Wd h_tj,
-    summed over j in slot order (mode mxfp8: h as two MXFP8 terms and every
+    summed over j in slot order (MXFP8 modes: h in its MX form and every
     slot contribution rounded to BF16, as in moe_layer)."""
+    _check_mode(act_quant)
     ids, w = slots(topk_ids, topk_weights, num_experts, num_shared)
-    hh = (F.fake_quant_mx_e4m3_two_term(h) if act_quant == "mxfp8"
-          else np.asarray(h, dtype=np.float64))
+    hh = quantise_h(h, act_quant)
     ys = None
     for e, rows, cols in _group(ids):
         _, _, wd = dequant_expert(fmt, get_expert(e))
         if ys is None:
             ys = np.zeros(ids.shape + (wd.shape[0],))
         contrib = (hh[rows, cols] @ wd.T) * w[rows, cols][:, None]
-        ys[rows, cols] = F.round_to_bf16(contrib) if act_quant == "mxfp8" else contrib
+        ys[rows, cols] = round_slot(contrib, act_quant)
     y = np.zeros((ids.shape[0], ys.shape[2]))
     for j in range(ids.shape[1]):
         y += ys[:, j]
@@ -174,21 +208,18 @@ def down(h, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert,
 def moe_layer(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared, get_expert,
               act_quant="none"):
     """y [T][H] float64 for the whole routed-expert FFN."""
-    if act_quant not in ("none", "mxfp8"):
-        raise ValueError(act_quant)
+    _check_mode(act_quant)
     ids, w = slots(topk_ids, topk_weights, num_experts, num_shared)
-    a = F.fake_quant_mx_e4m3(x) if act_quant == "mxfp8" else x
+    a = quantise_x(x, act_quant)
     ys = None
     for e, rows, cols in _group(ids):
         wg, wu, wd = dequant_expert(fmt, get_expert(e))
         xa = a[rows]
-        hh = silu(xa @ wg.T) * (xa @ wu.T)
-        if act_quant == "mxfp8":
-            hh = F.fake_quant_mx_e4m3_two_term(hh)
+        hh = quantise_h(silu(xa @ wg.T) * (xa @ wu.T), act_quant)
         if ys is None:
             ys = np.zeros(ids.shape + (wd.shape[0],))
         contrib = (hh @ wd.T) * w[rows, cols][:, None]
-        ys[rows, cols] = F.round_to_bf16(contrib) if act_quant == "mxfp8" else contrib
+        ys[rows, cols] = round_slot(contrib, act_quant)
     y = np.zeros((ids.shape[0], ys.shape[2]))
     for j in range(ids.shape[1]):
         y += ys[:, j]
@@ -203,14 +234,14 @@ def moe_layer_scalar(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared,
                      act_quant="none"):
     """Same definition as ``moe_layer`` written as plain Python loops over
     tokens, slots, neurons and outputs with math.fsum; for tiny shapes."""
+    _check_mode(act_quant)
     ids, w = slots(topk_ids, topk_weights, num_experts, num_shared)
     t_n, s_n = ids.shape
     cache = {}
     rows = []
     for t in range(t_n):
         xt = [float(v) for v in x[t]]
-        if act_quant == "mxfp8":
-            xt = [float(v) for v in F.fake_quant_mx_e4m3(np.array(xt))]
+        xt = [float(v) for v in quantise_x(np.array(xt), act_quant)]
         contrib = []
         for j in range(s_n):
             e = int(ids[t, j])
@@ -223,12 +254,10 @@ def moe_layer_scalar(x, topk_ids, topk_weights, *, fmt, num_experts, num_shared,
                 g = math.fsum(wg[n, c] * xt[c] for c in range(n_h))
                 u = math.fsum(wu[n, c] * xt[c] for c in range(n_h))
                 h.append(g / (1.0 + math.exp(-g)) * u)
-            if act_quant == "mxfp8":
-                h = [float(v) for v in F.fake_quant_mx_e4m3_two_term(np.array(h))]
+            h = [float(v) for v in quantise_h(np.array(h), act_quant)]
             c = [w[t, j] * math.fsum(wd[d, n] * h[n] for n in range(n_i))
                  for d in range(wd.shape[0])]
-            if act_quant == "mxfp8":
-                c = [float(v) for v in F.round_to_bf16(np.array(c))]
+            c = [float(v) for v in round_slot(np.array(c), act_quant)]
             contrib.append(c)
         rows.append([math.fsum(c[d] for c in contrib) for d in range(len(contrib[0]))])
     return np.array(rows, dtype=np.float64)

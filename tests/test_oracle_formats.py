@@ -162,6 +162,41 @@ def test_two_term_mx_quantisation():
     assert np.abs(hi - v).max() > np.abs(approx - v).max()
 
 
+def test_two_term_lo_term_scale_rule():
+    """The second term is an MX quantisation of the residual r = v - hi with
+    its own shared exponent, floor(log2 max|r|) - 8 (numpy log2, clamped,
+    -127 for an all-zero residual block), and codes equal to torch's
+    float8_e4m3fn cast of clip(r / 2^e, +-448): checked against the
+    independent route, with blocks spanning many magnitudes, exactly
+    representable blocks (zero residual) and an all-zero block."""
+    import _torch_route as R
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((48, 256)) * np.exp(rng.uniform(-30, 30, (48, 1)))
+    v[5] = 0.0                                            # all-zero blocks
+    v[6] = np.ldexp(np.round(rng.uniform(-8, 8, 256)), 3)  # exact in E4M3: zero residual
+    v[7, :32] = 448.0 * 2.0 ** 3                          # saturating block maximum
+    ch, sh, cl, sl = F.quantize_mx_e4m3_two_term(v)
+    rc, rs = R.mx_quant(v)
+    assert np.array_equal(ch, rc) and np.array_equal(sh, rs)
+    r = v - R.mx_dequant_e4m3(rc, rs)
+    lc, ls = R.mx_quant(r)
+    assert np.array_equal(sl, ls) and np.array_equal(cl, lc)
+    ramax = np.abs(r).reshape(48, 8, 32).max(-1)
+    want = np.where(ramax > 0, np.clip(np.floor(np.log2(np.where(ramax > 0, ramax, 1))) - 8,
+                                       -127, 127), -127) + 127
+    assert np.array_equal(sl.astype(np.int64), want.astype(np.int64))
+    assert np.all(sl[6] == 0) and np.all(cl[6] & 0x7F == 0)
+    # lo has its own exponent: at least three binades below hi's wherever the
+    # block is non-zero, so a quantiser that encoded lo on hi's shared
+    # exponent would fail the equalities above
+    nz = (np.abs(v).reshape(48, 8, 32).max(-1) > 0) & (ramax > 0)
+    assert np.all(sl.astype(np.int64)[nz] <= sh.astype(np.int64)[nz] - 3)
+    e_hi = sh.astype(np.int64) - 127
+    on_hi = np.clip(r.reshape(48, 8, 32) / np.exp2(e_hi.astype(np.float64))[..., None], -448, 448)
+    codes_on_hi = torch.from_numpy(on_hi).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert not np.array_equal(codes_on_hi.reshape(48, 256), cl)
+
+
 def test_round_to_bf16_vs_torch_and_ties():
     """float32 inputs: equal to torch's float32 -> bfloat16 cast (RNE);
     exact halfway cases go to the even significand; idempotent."""

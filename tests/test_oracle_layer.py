@@ -39,7 +39,7 @@ def _kw(cfg, getter=None):
 
 
 @pytest.mark.parametrize("fmt", list(TINY))
-@pytest.mark.parametrize("mode", ["none", "mxfp8"])
+@pytest.mark.parametrize("mode", ["none", "mxfp8", "mxfp8_single"])
 def test_vectorised_matches_scalar_brute_force(fmt, mode):
     cfg = TINY[fmt]
     t = 3 if fmt != "f32" else 4
@@ -190,3 +190,45 @@ def test_mxfp8_mode_quantises_activations():
     assert np.allclose(L.moe_layer(x, ids, w, act_quant="mxfp8", **kw), y_ref, rtol=0, atol=1e-13)
     # and it differs from mode none (the quantisation is really applied)
     assert not np.allclose(L.moe_layer(x, ids, w, **kw), y_ref, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("fmt,shared", [("mxfp8", 0), ("mxfp4", 0), ("fp8_blk128", 0),
+                                        ("fp8_blk128", 1), ("f32", 0)])
+@pytest.mark.parametrize("mode,terms", [("mxfp8", 2), ("mxfp8_single", 1)])
+def test_expert_centric_modes_match_an_independent_route(fmt, shared, mode, terms):
+    """The MXFP8 modes' whole composition -- x quantised per 32 along H, h
+    requantised per 32 along I with one or two terms, every slot's weighted
+    output rounded to BF16, then the slot-order sum -- recomputed token by
+    token through torch's float8_e4m3fn / float8_e8m0fnu / bfloat16 casts,
+    numpy's log2, the OCP E2M1 table and torch float64 silu and matmul
+    (tests/_torch_route.py, which does not import the oracle)."""
+    import _torch_route as R
+    cfg = TINY[fmt].replace(num_shared=shared)
+    t = 4 if fmt != "f32" else 3
+    x, ids, w = _inputs(cfg, t)
+    get = _getter(cfg)
+    y = L.moe_layer(x, ids, w, act_quant=mode, **_kw(cfg, getter=get))
+    ref = R.expert_centric_layer(x, ids, w, fmt=cfg.fmt, num_experts=cfg.num_experts,
+                                 num_shared=shared, get_expert=get, terms=terms)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref)), (fmt, mode)
+    # the other term count is measurably different: the pin tells them apart
+    other = R.expert_centric_layer(x, ids, w, fmt=cfg.fmt, num_experts=cfg.num_experts,
+                                   num_shared=shared, get_expert=get, terms=3 - terms)
+    assert np.max(np.abs(other - ref)) > 1e-6 * np.max(np.abs(ref))
+
+
+def test_mxfp8_modes_are_the_documented_steps_of_each_other():
+    """Mode mxfp8_single differs from mxfp8 only in the requantisation of h;
+    the two-term form is within 2^-6 of each block maximum of h, the
+    single-term one within 2^-4 relative of each normal element, so the
+    two-term mode lies closer to the unquantised-h layer on Q(x)."""
+    cfg = TINY["mxfp8"]
+    x, ids, w = _inputs(cfg, 6)
+    kw = _kw(cfg)
+    xq = F.fake_quant_mx_e4m3(x)
+    exact_h = L.moe_layer(xq, ids, w, **kw)          # Q(x), exact h, FP64 slots
+    y1 = L.moe_layer(x, ids, w, act_quant="mxfp8_single", **kw)
+    y2 = L.moe_layer(x, ids, w, act_quant="mxfp8", **kw)
+    e1 = np.linalg.norm(y1 - exact_h) / np.linalg.norm(exact_h)
+    e2 = np.linalg.norm(y2 - exact_h) / np.linalg.norm(exact_h)
+    assert e2 < e1 / 4, (e1, e2)
