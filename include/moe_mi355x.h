@@ -235,7 +235,8 @@ moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H
  *   hq      device [2][capacity][I] E4M3 (hi rows, then lo rows)
  *   hs      device [2][capacity][I/32] E8M0
  * Weight formats: MOE_W_MXFP8, MOE_W_MXFP4, MOE_W_FP8_BLK128.
- * block_size in {32, 64, 128}; H multiple of 128; I multiple of 64.
+ * block_size in {32, 64, 128}; H and I multiples of 128 (MOE_ERR_UNSUPPORTED
+ * otherwise).
  */
 moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const uint8_t* xs,
                                const int32_t* expert_ids,

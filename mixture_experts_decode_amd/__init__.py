@@ -6,7 +6,9 @@ nothing else of torch is used here.  The library must be built
 (``python -m mixture_experts_decode_amd.build``); without it every call raises.
 """
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -101,6 +103,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a binding call with its `stream` argument made torch's current
+    stream, so every tensor the call allocates (outputs, scratch) belongs to
+    the stream its kernels are enqueued on and the caching allocator does not
+    hand that memory to other work while they run."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kwargs):
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapped
+
+
 class Weights:
     """One layer's expert weights resident on the device.
 
@@ -150,6 +165,7 @@ def _alloc(shape, dtype, device):
     return torch.empty(shape, dtype=tdt, device=device)
 
 
+@_on_stream
 def gate_up(W, x, topk_ids, h=None, h_dtype="f32", stream=None):
     """h [T][k+S][I] for the decode path."""
     load()
@@ -162,6 +178,7 @@ def gate_up(W, x, topk_ids, h=None, h_dtype="f32", stream=None):
     return h
 
 
+@_on_stream
 def down(W, h, topk_ids, topk_weights, y=None, y_dtype="f32", variant="auto", workspace=None,
          stream=None):
     """y [T][H] for the decode path.  variant: "token" (no workspace),
@@ -190,6 +207,7 @@ def align_sort_capacity(t, k, num_experts, num_shared, block):
     return _lib.moe_align_sort_capacity(t, k, num_experts, num_shared, block)
 
 
+@_on_stream
 def align_sort(topk_ids, num_experts, num_shared, block, stream=None):
     """Returns dict of device tensors: sorted_token_ids [cap], expert_ids
     [cap/bs], expert_offsets [E+S+1], num_tokens_post_padded [1]."""
@@ -215,6 +233,7 @@ def align_sort(topk_ids, num_experts, num_shared, block, stream=None):
     return out
 
 
+@_on_stream
 def gather_quant(x, slots, sorted_ids, npp, capacity, stream=None):
     load()
     t, h = x.shape
@@ -226,6 +245,7 @@ def gather_quant(x, slots, sorted_ids, npp, capacity, stream=None):
     return xq, xs
 
 
+@_on_stream
 def grouped_gate_up(W, xq, xs, expert_ids, npp, capacity, block, stream=None):
     load()
     hq = torch.empty((2, capacity, W.inter), dtype=torch.uint8, device=xq.device)
@@ -236,6 +256,7 @@ def grouped_gate_up(W, xq, xs, expert_ids, npp, capacity, block, stream=None):
     return hq, hs
 
 
+@_on_stream
 def grouped_down(W, hq, hs, sorted_ids, expert_ids, npp, capacity, block, topk_weights, t, k,
                  slot_out=None, stream=None):
     load()
@@ -251,6 +272,7 @@ def grouped_down(W, hq, hs, sorted_ids, expert_ids, npp, capacity, block, topk_w
     return slot_out
 
 
+@_on_stream
 def combine(slot_out, t, slots, y=None, y_dtype="f32", stream=None):
     load()
     if slot_out.dtype != torch.bfloat16:
@@ -263,6 +285,7 @@ def combine(slot_out, t, slots, y=None, y_dtype="f32", stream=None):
     return y
 
 
+@_on_stream
 def topk_route(scores, k, bias=None, ids=None, wts=None, stream=None):
     """Router front-end: scores [T][E] float32 (device), bias [E] or None ->
     (topk_ids int32 [T][k], topk_weights float32 [T][k]), written into ids /
@@ -289,6 +312,7 @@ def layer_workspace_bytes(W, t, k, path="auto", block=0):
     return _lib.moe_layer_workspace_bytes(W.ref, t, k, PATH[path], block)
 
 
+@_on_stream
 def layer(W, x, topk_ids, topk_weights, path="auto", block=0, y=None, y_dtype="f32",
           workspace=None, stream=None):
     """y [T][H] for the whole layer; returns (y, path that ran)."""

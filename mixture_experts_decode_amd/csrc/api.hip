@@ -338,11 +338,12 @@ moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int
 }
 
 int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
-  if (check_weights(W) != MOE_OK || T < 0 || k < 0) return MOE_PATH_DECODE;
-  const int64_t entries = (int64_t)T * (k + W->num_shared);
-  if (!grouped_supported(W)) return MOE_PATH_DECODE;
-  if (W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;
-  if (entries > kDecodeMaxEntries) return MOE_PATH_GROUPED;
+  if (check_weights(W) != MOE_OK || check_routing(W, T, k) != MOE_OK) return MOE_PATH_DECODE;
+  if (!grouped_supported(W) || W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;
+  // a path the decode kernels refuse (too many entries to stage on chip, more
+  // than 64 slots, a row length with no compiled shape) is never picked
+  if (moe::decode_supported(*W, T, k, decode_h_dtype(W), moe::down_expert_major(T)) != hipSuccess)
+    return MOE_PATH_GROUPED;
   return model_path(W, T, k);
 }
 
@@ -376,13 +377,16 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   const int32_t slots = k + W->num_shared;
   if (path == MOE_PATH_DECODE) {
     if (workspace_bytes < decode_workspace(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+    if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
     const int32_t hdt = decode_h_dtype(W);
+    // expert-major down from a few tokens up (identical results either way)
+    const bool em = moe::down_expert_major(T);
+    // every shape limit of both kernels is checked before the first launch
+    if (moe::decode_supported(*W, T, k, hdt, em) != hipSuccess) return MOE_ERR_UNSUPPORTED;
     st = moe_gate_up(W, x, x_dtype, topk_ids, T, k, workspace, hdt, stream);
     if (st != MOE_OK) return st;
-    // expert-major down from a few tokens up (identical results either way)
     char* so = reinterpret_cast<char*>(workspace) + decode_h_bytes(W, T, k);
-    const bool em = moe::down_expert_major(T);
     return moe_down(W, workspace, hdt, topk_ids, topk_weights, T, k, y, y_dtype,
                     em ? so : nullptr, em ? workspace_bytes - decode_h_bytes(W, T, k) : 0,
                     stream);

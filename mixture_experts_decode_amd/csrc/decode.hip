@@ -32,7 +32,7 @@
 //    chunk's partial sum, except in gate_up rows converted once per item,
 //    where an MX scale (a power of two) enters the conversion itself.
 
-#include <cstdlib>
+#include <algorithm>
 
 #include "device.h"
 #include "internal.h"
@@ -655,10 +655,44 @@ hipError_t down_shape(const DownArgs& a, int lpr, bool em, int ybf16, int blocks
 
 }  // namespace
 
-hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
-                                 const int32_t* ids, int T, int k, void* h, int h_dtype,
-                                 hipStream_t s) {
+// ---- host planning: every refusal is decided here, before any launch -----
+
+namespace {
+
+int lanes_per_row_for(int fmt, int inter, int h_dtype) {
+  const int chunks = row_bytes_of(fmt, inter) / 16;
+  const int elems = fmt == W_F32 ? 4 : fmt == W_MXFP4 ? 32 : 16;
+  const int hwords = elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
+  auto inst = [&](int lpr) {
+    if (chunks % lpr) return false;
+    const int c = chunks / lpr;
+    return c == 2 || c == 3 || c == 4 || c == 6 || c == 8 || c == 12 || c == 16;
+  };
+  for (int lpr : {4, 8, 16, 32}) {
+    const int c = chunks / lpr;
+    if (inst(lpr) && (lpr >= 8 || chunks < 16) && 2 * c * 5 + c * hwords <= 80) return lpr;
+  }
+  for (int budget = 48; budget <= 128; budget *= 2)
+    for (int lpr : {4, 8, 16, 32})
+      if (inst(lpr) && (lpr >= 8 || chunks < 16) && (chunks / lpr) * hwords <= budget) return lpr;
+  return 0;
+}
+
+struct GateUpPlan {
   GateUpArgs a;
+  int nr, mch, blocks;
+  bool pre, guard;
+};
+
+struct DownPlan {
+  DownArgs a;
+  int lpr, blocks;
+  bool em;
+};
+
+hipError_t plan_gate_up(const moe_weights& W, const void* x, const int32_t* ids, int T, int k,
+                        void* h, GateUpPlan& p) {
+  GateUpArgs& a = p.a;
   a.w13 = reinterpret_cast<const uint8_t*>(W.w13);
   a.w13s = W.w13_scale;
   a.x = x;
@@ -675,29 +709,42 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
   a.n_entries = T * a.slots;
+  if (a.n_entries > kDecodeMaxEntries) return hipErrorNotSupported;
   // chunks per lane: exact when the row is a whole number of 64-lane passes
   // (loads then batch without guards), else the next instantiated size
   const int lane_chunks = (a.chunks + kWave - 1) / kWave;
-  const bool guard = a.chunks % kWave != 0 ||
-                     !(lane_chunks == 1 || lane_chunks == 2 || lane_chunks == 4 ||
-                       lane_chunks == 7 || lane_chunks == 8);
-  const int mch = !guard ? lane_chunks
-                         : lane_chunks <= 1 ? 1 : lane_chunks <= 2 ? 2 : lane_chunks <= 4 ? 4 : 8;
   if (lane_chunks > 8) return hipErrorNotSupported;
+  p.guard = a.chunks % kWave != 0 ||
+            !(lane_chunks == 1 || lane_chunks == 2 || lane_chunks == 4 || lane_chunks == 7 ||
+              lane_chunks == 8);
+  p.mch = !p.guard ? lane_chunks
+                   : lane_chunks <= 1 ? 1 : lane_chunks <= 2 ? 2 : lane_chunks <= 4 ? 4 : 8;
   // neurons per wavefront: two while the rows stay small in registers; rows
   // converted to BF16 once per item while that takes at most 64 VGPRs
-  const int nr = mch <= 2 ? env_int("MOE_TUNE_GU_NR", 2) == 1 ? 1 : 2 : 1;
+  p.nr = p.mch <= 2 ? 2 : 1;
   const int elems = W.format == W_MXFP4 ? 32 : 16;
-  const bool pre = W.format != W_F32 && mch <= 4 &&
-                   env_int("MOE_TUNE_GU_PRE", 2 * nr * mch * elems / 2 <= 64 ? 1 : 0) != 0;
+  p.pre = W.format != W_F32 && p.mch <= 4 && 2 * p.nr * p.mch * elems / 2 <= 64;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
-  a.n_groups = (W.inter + nr - 1) / nr;
+  a.n_groups = (W.inter + p.nr - 1) / p.nr;
   const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_groups;
   const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int cap = device_num_cus() * env_int("MOE_TUNE_GU_BPC", 16);
-  const int blocks = (int)std::max<long long>(1, std::min<long long>(want, cap));
+  p.blocks = (int)std::max<long long>(1, std::min<long long>(want, device_num_cus() * 16LL));
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
+                                 const int32_t* ids, int T, int k, void* h, int h_dtype,
+                                 hipStream_t s) {
+  GateUpPlan p;
+  hipError_t e = plan_gate_up(W, x, ids, T, k, h, p);
+  if (e != hipSuccess) return e;
+  const GateUpArgs& a = p.a;
   const bool xf32 = x_dtype == MOE_DT_F32;
   const bool hbf = h_dtype == MOE_DT_BF16;
+  const int nr = p.nr, mch = p.mch, blocks = p.blocks;
+  const bool pre = p.pre, guard = p.guard;
   switch (W.format) {
     case W_F32:
       if (xf32) return hbf ? gate_up_nr<W_F32, true, true>(a, nr, pre, mch, guard, blocks, s)
@@ -725,32 +772,16 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
 // (weights + scales ~5 VGPRs per chunk, plus the staged h chunks); failing
 // that, one row per group with at most 48 (then 96) VGPRs of h.  0 if none.
 int down_lanes_per_row(int fmt, int inter, int h_dtype) {
-  const int chunks = row_bytes_of(fmt, inter) / 16;
-  const int elems = fmt == W_F32 ? 4 : fmt == W_MXFP4 ? 32 : 16;
-  const int hwords = elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
-  auto inst = [&](int lpr) {
-    if (chunks % lpr) return false;
-    const int c = chunks / lpr;
-    return c == 2 || c == 3 || c == 4 || c == 6 || c == 8 || c == 12 || c == 16;
-  };
-  const int forced = env_int("MOE_TUNE_DN_LPR", 0);
-  if (forced && inst(forced)) return forced;
-  for (int lpr : {4, 8, 16, 32}) {
-    const int c = chunks / lpr;
-    if (inst(lpr) && (lpr >= 8 || chunks < 16) && 2 * c * 5 + c * hwords <= 80) return lpr;
-  }
-  for (int budget = 48; budget <= 128; budget *= 2)
-    for (int lpr : {4, 8, 16, 32})
-      if (inst(lpr) && (lpr >= 8 || chunks < 16) && (chunks / lpr) * hwords <= budget) return lpr;
-  return 0;
+  return lanes_per_row_for(fmt, inter, h_dtype);
 }
 
-bool down_expert_major(int T) { return T >= env_int("MOE_TUNE_DN_EM_MIN_T", 4); }
+bool down_expert_major(int T) { return T >= 4; }
 
-hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
-                              const int32_t* ids, const float* wts, int T, int k, void* y,
-                              int y_dtype, float* slot_out, hipStream_t s) {
-  DownArgs a;
+namespace {
+
+hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int32_t* ids,
+                     const float* wts, int T, int k, void* y, float* slot_out, DownPlan& p) {
+  DownArgs& a = p.a;
   a.w2 = reinterpret_cast<const uint8_t*>(W.w2);
   a.w2s = W.w2_scale;
   a.h = h;
@@ -764,63 +795,89 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
   a.I = W.inter;
   a.row_bytes = row_bytes_of(W.format, W.inter);
   a.chunks = a.row_bytes / 16;
-  const int lpr = down_lanes_per_row(W.format, W.inter, h_dtype);
-  if (lpr == 0) return hipErrorNotSupported;
+  p.em = slot_out != nullptr;
+  // one slot per lane in the token-major kernel
+  if (a.slots > kWave) return hipErrorNotSupported;
+  p.lpr = lanes_per_row_for(W.format, W.inter, h_dtype);
+  if (p.lpr == 0) return hipErrorNotSupported;
   // row offsets inside one expert are 32-bit in the kernels
   if ((long long)a.H * a.row_bytes >= (1ll << 32)) return hipErrorNotSupported;
-  a.cpl = a.chunks / lpr;
-  const int nd = kWave / lpr;
+  a.n_entries = T * a.slots;
+  // the expert-major kernel stages the routed ids on chip
+  if (p.em && a.n_entries > kDecodeMaxEntries) return hipErrorNotSupported;
+  a.cpl = a.chunks / p.lpr;
+  const int nd = kWave / p.lpr;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
-  const bool em_launch = slot_out != nullptr;
-  // two or four rows per lane group in the expert-major kernel: more bytes
-  // in flight per item, each staged h chunk used for every row
+  // two or four rows per lane group in the expert-major kernel (more bytes in
+  // flight per item, each staged h chunk used for every row) as the register
+  // budget allows, within the compiled shapes
   const int elems = W.format == W_F32 ? 4 : W.format == W_MXFP4 ? 32 : 16;
   const int hregs = a.cpl * elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
   const int rpl_fit = 4 * a.cpl * 5 + hregs <= 96 ? 4 : 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1;
-  const int rpl_max = a.cpl <= 3 ? 4 : a.cpl <= 4 ? 2 : 1;   // compiled shapes
-  a.rpl = em_launch ? std::min(env_int("MOE_TUNE_DN_RPL", rpl_fit), rpl_max) : 1;
+  const int rpl_max = a.cpl <= 3 ? 4 : a.cpl <= 4 ? 2 : 1;
+  a.rpl = p.em ? std::min(rpl_fit, rpl_max) : 1;
   a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
-  a.n_entries = T * a.slots;
   a.nxcd = device_num_xcds();
-  const bool hbf = h_dtype == MOE_DT_BF16;
-  const int ybf = y_dtype == MOE_DT_BF16;
-  const bool em = slot_out != nullptr;
-  int blocks;
-  if (em) {
+  if (p.em) {
     a.y = slot_out;
     const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_dgroups;
     const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int cap = device_num_cus() * env_int("MOE_TUNE_DN_BPC", 8);
-    blocks = (int)std::max<long long>(1, std::min<long long>(want, cap));
+    p.blocks = (int)std::max<long long>(1, std::min<long long>(want, device_num_cus() * 8LL));
   } else {
     a.y = y;
-    blocks = T * a.n_dgroups;              // one workgroup per (token, output group)
+    const long long blocks = (long long)T * a.n_dgroups;   // one workgroup per (token, output group)
+    if (blocks > 0x7fffffffLL) return hipErrorNotSupported;
+    p.blocks = (int)blocks;
   }
-  hipError_t err;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
+                              const int32_t* ids, const float* wts, int T, int k, void* y,
+                              int y_dtype, float* slot_out, hipStream_t s) {
+  DownPlan p;
+  hipError_t err = plan_down(W, h, h_dtype, ids, wts, T, k, y, slot_out, p);
+  if (err != hipSuccess) return err;
+  const DownArgs& a = p.a;
+  const bool hbf = h_dtype == MOE_DT_BF16;
+  const int ybf = y_dtype == MOE_DT_BF16;
+  const bool em = p.em;
   switch (W.format) {
     case W_F32:
-      err = hbf ? down_shape<W_F32, true>(a, lpr, em, ybf, blocks, s)
-                : down_shape<W_F32, false>(a, lpr, em, ybf, blocks, s);
+      err = hbf ? down_shape<W_F32, true>(a, p.lpr, em, ybf, p.blocks, s)
+                : down_shape<W_F32, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     case W_MXFP8:
-      err = hbf ? down_shape<W_MXFP8, true>(a, lpr, em, ybf, blocks, s)
-                : down_shape<W_MXFP8, false>(a, lpr, em, ybf, blocks, s);
+      err = hbf ? down_shape<W_MXFP8, true>(a, p.lpr, em, ybf, p.blocks, s)
+                : down_shape<W_MXFP8, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     case W_MXFP4:
-      err = hbf ? down_shape<W_MXFP4, true>(a, lpr, em, ybf, blocks, s)
-                : down_shape<W_MXFP4, false>(a, lpr, em, ybf, blocks, s);
+      err = hbf ? down_shape<W_MXFP4, true>(a, p.lpr, em, ybf, p.blocks, s)
+                : down_shape<W_MXFP4, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     case W_FP8B128:
-      err = hbf ? down_shape<W_FP8B128, true>(a, lpr, em, ybf, blocks, s)
-                : down_shape<W_FP8B128, false>(a, lpr, em, ybf, blocks, s);
+      err = hbf ? down_shape<W_FP8B128, true>(a, p.lpr, em, ybf, p.blocks, s)
+                : down_shape<W_FP8B128, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     default:
       return hipErrorInvalidValue;
   }
   if (err != hipSuccess || !em) return err;
   return launch_combine(slot_out, MOE_DT_F32, T, a.slots, W.hidden, y, y_dtype, s);
+}
+
+hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype, bool expert_major) {
+  GateUpPlan g;
+  hipError_t e = plan_gate_up(W, nullptr, nullptr, T, k, nullptr, g);
+  if (e != hipSuccess) return e;
+  DownPlan d;
+  static float dummy;
+  return plan_down(W, nullptr, h_dtype, nullptr, nullptr, T, k, nullptr,
+                   expert_major ? &dummy : nullptr, d);
 }
 
 }  // namespace moe

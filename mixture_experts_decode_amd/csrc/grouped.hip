@@ -725,10 +725,8 @@ hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
     // at 32-row blocks (Qwen3 B = 64: 48.9 -> 46.4 us; MXFP4: 125.6 ->
     // 113 us), while the FP8 128x128 layer was 5% slower (553 -> 582 us)
     if constexpr (!GATEUP && BFMT != W_FP8B128) {
-      if (env_int("MOE_TUNE_GG_DN512", 1)) {
-        MOE_GG(32, 512, 1, 8, 2);
-        return hipGetLastError();
-      }
+      MOE_GG(32, 512, 1, 8, 2);
+      return hipGetLastError();
     }
     MOE_GG(32, 256, 1, 4, 2);
   } else if (bs == 64) {

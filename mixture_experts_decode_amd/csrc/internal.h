@@ -15,9 +15,6 @@ constexpr int kMaxExpertsTotal = 1024;    // E + S
 
 int device_num_cus();
 int device_num_xcds();
-// integer launch-shape override from the environment (measurement sweeps);
-// dflt when unset
-int env_int(const char* name, int dflt);
 
 // decode.hip
 hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
@@ -30,6 +27,9 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               int y_dtype, float* slot_out, hipStream_t s);
 int down_lanes_per_row(int fmt, int inter, int h_dtype);
 bool down_expert_major(int T);
+// hipSuccess if both decode kernels accept this shape (the down kernel in the
+// expert-major variant or not), else hipErrorNotSupported; launches nothing
+hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype, bool expert_major);
 
 // align_sort.hip
 size_t align_sort_workspace_bytes(int n_entries, int n_experts);

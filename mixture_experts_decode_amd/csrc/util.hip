@@ -4,7 +4,6 @@
 // compute-unit count cache.
 
 #include <atomic>
-#include <cstdlib>
 
 #include "device.h"
 #include "internal.h"
@@ -64,11 +63,6 @@ int device_num_cus() {
 
 // gfx950 parts (MI350 series) are built from 8 accelerator complex dies.
 int device_num_xcds() { return 8; }
-
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return v ? std::atoi(v) : dflt;
-}
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 16;

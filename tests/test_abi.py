@@ -158,3 +158,46 @@ def test_path_choice_host_logic(lib):
     for t, bs in ((32, 32), (1024, 64), (16384, 128)):
         assert (lib.moe_layer_workspace_bytes(ctypes.byref(w), t, 8, GRP, 0) ==
                 lib.moe_layer_workspace_bytes(ctypes.byref(w), t, 8, GRP, bs))
+
+
+def test_layer_refuses_unsupported_decode_shapes_before_any_launch(lib):
+    """Every decode-kernel limit is checked before the first launch: on a
+    host without a GPU a call that reached a launch would return
+    MOE_ERR_HIP, so MOE_ERR_UNSUPPORTED proves nothing was enqueued."""
+    moe = __import__("mixture_experts_decode_amd")
+    P = ctypes.c_void_p
+    dummy = P(4096)
+    big = 1 << 40
+    DEC, GRP = 1, 2
+    # a W_down row of 64 E4M3 bytes has no compiled lane split
+    narrow = _weights(moe, inter=64)
+    assert lib.moe_layer(ctypes.byref(narrow), dummy, 1, dummy, dummy, 4, 8, dummy, 0, DEC, 0,
+                         dummy, big, None, None) == moe.ERR_UNSUPPORTED
+    # no grouped path for it either (I is not a multiple of 128): AUTO keeps
+    # decode and the call is refused the same way
+    assert lib.moe_choose_path(ctypes.byref(narrow), 4, 8) == DEC
+    assert lib.moe_layer(ctypes.byref(narrow), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 0, 0,
+                         dummy, big, None, None) == moe.ERR_UNSUPPORTED
+    # more than 64 slots: the token-major down kernel keeps one slot per lane
+    w = _weights(moe)
+    assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 2, 65, dummy, 0, DEC, 0,
+                         dummy, big, None, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_down(ctypes.byref(w), dummy, 1, dummy, dummy, 2, 65, dummy, 0, None, 0,
+                        None) == moe.ERR_UNSUPPORTED
+    # AUTO never picks a path that cannot run
+    assert lib.moe_choose_path(ctypes.byref(w), 2, 65) == GRP
+    # more entries than the decode kernels stage on chip
+    assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 257, 8, dummy, 0, DEC, 0,
+                         dummy, big, None, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_choose_path(ctypes.byref(w), 257, 8) == GRP
+    # F32 activations with quantised weights, refused by moe_layer itself
+    assert lib.moe_layer(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, DEC, 0,
+                         dummy, big, None, None) == moe.ERR_UNSUPPORTED
+
+
+def test_library_reads_no_tuning_environment(lib):
+    """Launch shapes are fixed in the library: it reads no environment
+    variables, so no setting can pick a shape that was not compiled."""
+    import mixture_experts_decode_amd as moe
+    blob = open(moe.LIB_PATH, "rb").read()
+    assert b"MOE_TUNE" not in blob and b"getenv" not in blob
