@@ -1,6 +1,6 @@
 """Benchmark of the routed-expert MoE FFN on one MI355X.
 
-Default workload: the Qwen3-style decode layer (hidden 2048, expert
+Headline workload: the Qwen3-style decode layer (hidden 2048, expert
 intermediate 768, 128 experts, top-8, MXFP8 weights, BF16 activations) at
 B = 32 tokens, run by moe_layer's path for that batch (the output-centric
 decode kernels).  One step = one layer call over one batch; consecutive steps
@@ -8,12 +8,18 @@ cycle through several independent copies of the layer's weights with their
 own routing draws (as the layers of a model do), so every step streams its
 experts from HBM rather than from a cache warmed by the previous step.
 
+Every timed configuration is first checked against the float64 oracle on the
+same inputs (per-token cosine, relative L2 and max-abs in the oracle mode of
+the path that ran), and the check is printed beside its time.
+
 Prints ONE JSON line: value = achieved HBM bandwidth in TB/s counted from the
 algorithmic bytes of each step's actual routing (each touched expert's weights
 and scales once, plus x, ids, routing weights and y), ms_per_step = time per
-layer.  Also: the measured copy-kernel peak and the fraction of it, a batch
-sweep, the dominant kernel's roofline entry, and the float64 oracle timed on
-the host cores (CPU baseline leg).
+layer.  Also: the measured copy-kernel peak and the fraction of it, the batch
+sweep B = 1-256 over the workloads (both paths where both run), the dominant
+kernel's roofline entry, the grouped path kernel by kernel with matrix-core
+utilisation, the accuracy of the two regimes against exact activations, and
+the float64 oracle timed on the host cores (CPU baseline leg).
 """
 
 import argparse
@@ -29,14 +35,16 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "µs per MoE layer & achieved HBM TB/s (fraction of peak), B=1–256, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 # MI355X published dense matrix-core peaks (TFLOP/s).  The grouped GEMMs
-# take MXFP8 activations as the A operand, so even with E2M1 weights every
+# take MXFP8 activations as one operand, so even with E2M1 weights every
 # block-scaled MFMA issues at the 8-bit rate.
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}
 DOMINANT = "gate_up_decode_kernel"
 KERNEL_SOURCES = ["mixture_experts_decode_amd/csrc/decode.hip",
                   "mixture_experts_decode_amd/csrc/device.h"]
+MODE = {"decode": "none", "grouped": "mxfp8"}
 
 
 def parse():
@@ -49,13 +57,14 @@ def parse():
     p.add_argument("--batch", type=int, default=32)
     p.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
     p.add_argument("--block", type=int, default=0)
-    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the B = 1-256 sweeps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-copy-peak", action="store_true")
     p.add_argument("--no-grouped", action="store_true",
-                   help="skip the expert-centric (grouped MFMA) report")
-    p.add_argument("--crossover", action="store_true",
-                   help="also sweep the MXFP4 layer over B with both paths")
+                   help="skip the expert-centric kernel-by-kernel report")
+    p.add_argument("--no-accuracy", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the headline workload (for profiler runs)")
     return p.parse_args()
 
 
@@ -80,6 +89,77 @@ def load_traffic(cfg_name, batch):
     return d.get("hbm_bytes_per_launch")
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def spread(values):
+    v = np.asarray(values, dtype=np.float64)
+    return {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.median(v)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2), "n": int(v.size)}
+
+
+def sample_rows(t, n):
+    if n is None or n >= t:
+        return list(range(t))
+    return sorted({int(v) for v in np.linspace(0, t - 1, n)})
+
+
+# ---------------------------------------------------------------------------
+# oracle access (test infrastructure: only the parity checks and the CPU
+# baseline leg below use it)
+# ---------------------------------------------------------------------------
+
+class Oracle:
+    """The float64 oracle over one workload's stored weights; each touched
+    expert is dequantised once and reused by every check of the run."""
+
+    def __init__(self, cfg, arrays, cache_bytes=8e9):
+        from oracle import layer as L
+        self.L, self.cfg, self.arrays = L, cfg, arrays
+        self.cache = {}
+        self.max_entries = max(8, int(cache_bytes // (3 * cfg.hidden * cfg.inter * 8)))
+
+    def _get(self, e):
+        if e not in self.cache:
+            raw = {k: (None if v is None else v[e]) for k, v in self.arrays.items()}
+            wg, wu, wd = self.L.dequant_expert(self.cfg.fmt, raw)
+            self.cache[e] = {"w13": np.stack([wg, wu]), "w2": wd}
+            if len(self.cache) > self.max_entries:
+                self.cache.pop(next(iter(self.cache)))
+        return self.cache[e]
+
+    def layer(self, x, ids, w, mode):
+        c = self.cfg
+        return self.L.moe_layer(self.L.activations_f64(x, c.act), ids, w, act_quant=mode,
+                                fmt="f64", num_experts=c.num_experts, num_shared=c.num_shared,
+                                get_expert=self._get)
+
+
+def metrics(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    cos = np.sum(y * ref, 1) / (np.linalg.norm(y, axis=1) * np.linalg.norm(ref, axis=1))
+    rel = np.linalg.norm(y - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    return {"min_cos": float(np.min(cos)), "max_rel_l2": float(np.max(rel)),
+            "rel_l2": float(np.linalg.norm(y - ref) / np.linalg.norm(ref)),
+            "max_abs": float(np.max(np.abs(y - ref)))}
+
+
+def parity(oracle, x, ids, w, rows, y_dev, path):
+    """Per-token check of the GPU output rows against the oracle in the mode
+    of the path that ran; pass = cosine >= 0.99999 and rel-L2 <= 5e-3."""
+    y = y_dev.double().cpu().numpy()[rows]
+    ref = oracle.layer(x[rows], ids[rows], w[rows], MODE[path])
+    m = metrics(y, ref)
+    ok = m["min_cos"] >= 0.99999 and m["max_rel_l2"] <= 5e-3
+    return {"tokens": len(rows), "mode": MODE[path], "min_cos": round(m["min_cos"], 8),
+            "max_rel_l2": float(f"{m['max_rel_l2']:.3e}"), "max_abs": float(f"{m['max_abs']:.3e}"),
+            "pass": bool(ok)}
+
+
+# ---------------------------------------------------------------------------
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -97,46 +177,13 @@ def main():
     cfg = W.CONFIGS[args.workload]
     B = args.batch
     stream = torch.cuda.current_stream()
+    ctx = dict(moe=moe, W=W, torch=torch, dev=dev, stream=stream)
 
-    # ---- weights: one generated layer, copied so steps rotate through
-    # independent memory (>= ~2.5 GB in total)
-    arrays = W.all_experts(cfg)
-    w0 = moe.Weights.from_arrays(cfg, arrays)
-    layer_bytes = w0.nbytes()
-    n_layers = max(2, min(16, math.ceil(2.5e9 / layer_bytes)))
-    layers = [w0]
-    for _ in range(n_layers - 1):
-        t = [None if a is None else a.clone() for a in w0.tensors]
-        layers.append(moe.Weights(cfg.fmt, cfg.hidden, cfg.inter, cfg.num_experts,
-                                  cfg.num_shared, *t))
-    ebytes = W.expert_bytes(cfg)
-    act_bytes = 2 if cfg.act == "bf16" else 4
-
-    def make_inputs(b, variant):
-        x = W.activations(cfg, b, variant)
-        ids, wts = W.routing(cfg, b, variant=variant)
-        xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
-              else torch.from_numpy(x)).to(dev)
-        u = len(W.touched_experts(cfg, ids))
-        io = b * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes + b * cfg.hidden * 4
-        gate_up_bytes = u * (ebytes - ebytes_down(cfg)) + b * cfg.hidden * act_bytes + ids.nbytes \
-            + b * (cfg.top_k + cfg.num_shared) * cfg.inter * (4 if cfg.fmt == "f32" else 2)
-        return dict(x=xd, ids=torch.from_numpy(ids).to(dev), wts=torch.from_numpy(wts).to(dev),
-                    bytes=u * ebytes + io, gate_up_bytes=gate_up_bytes, U=u)
-
-    def ebytes_down(c):
-        shapes = W.weight_shapes(c)
-        tot = 0
-        for k in ("w2", "w2_scale"):
-            if k in shapes:
-                s, d = shapes[k]
-                tot += int(np.prod(s[1:])) * np.dtype(d).itemsize
-        return tot
-
-    # ---- copy peak (read + write bytes), best of 20, 2 GiB each way
+    # ---- copy peak (read + write bytes) and read-only peak, best of 20,
+    # 4 GiB each way
     copy_peak = read_peak = None
     if not args.no_copy_peak:
-        n = 2 << 30
+        n = 4 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty(n, dtype=torch.uint8, device=dev)
         moe.util_fill(src, n, 0x3c3c3c3c)
@@ -155,20 +202,51 @@ def main():
         copy_peak = 2 * n / (best_c * 1e-3) / 1e12
         read_peak = n / (best_r * 1e-3) / 1e12
         del src, dst
+        torch.cuda.empty_cache()
+        log(f"copy peak {copy_peak:.3f} TB/s, read peak {read_peak:.3f} TB/s (4 GiB)")
+    ctx["copy_peak"] = copy_peak
+
+    # ---- headline: weights copied so steps rotate through independent
+    # memory (>= ~2.5 GB in total)
+    arrays = W.all_experts(cfg)
+    oracle = Oracle(cfg, arrays)
+    w0 = moe.Weights.from_arrays(cfg, arrays)
+    layer_bytes = w0.nbytes()
+    n_layers = max(2, min(16, math.ceil(2.5e9 / layer_bytes)))
+    layers = [w0]
+    for _ in range(n_layers - 1):
+        t = [None if a is None else a.clone() for a in w0.tensors]
+        layers.append(moe.Weights(cfg.fmt, cfg.hidden, cfg.inter, cfg.num_experts,
+                                  cfg.num_shared, *t))
+    ebytes = W.expert_bytes(cfg)
+    ebytes_dn = down_expert_bytes(W, cfg)
+    act_bytes = 2 if cfg.act == "bf16" else 4
+    slots = cfg.top_k + cfg.num_shared
+
+    def make_inputs(b, variant):
+        x = W.activations(cfg, b, variant)
+        ids, wts = W.routing(cfg, b, variant=variant)
+        u = len(W.touched_experts(cfg, ids))
+        io = b * cfg.hidden * act_bytes + ids.nbytes + wts.nbytes + b * cfg.hidden * 4
+        h_el = 4 if cfg.fmt == "f32" else 2
+        gate_up_bytes = u * (ebytes - ebytes_dn) + b * cfg.hidden * act_bytes + ids.nbytes \
+            + b * slots * cfg.inter * h_el
+        return dict(x=to_dev_x(torch, dev, cfg, x), ids=torch.from_numpy(ids).to(dev),
+                    wts=torch.from_numpy(wts).to(dev), bytes=u * ebytes + io,
+                    gate_up_bytes=gate_up_bytes, U=u, np=(x, ids, wts))
 
     h_dtype = "f32" if cfg.fmt == "f32" else "bf16"   # as moe_layer's decode path
 
-    def run_steps(b, steps, warmup, path):
+    def run_steps(b, steps, warmup, path, n_check=None, replays=5):
         ins = [make_inputs(b, v) for v in range(n_layers)]
-        need = moe.layer_workspace_bytes(layers[0], b, cfg.top_k, path, args.block)
+        chosen = moe.choose_path(layers[0], b, cfg.top_k) if path == "auto" else path
+        need = moe.layer_workspace_bytes(layers[0], b, cfg.top_k, chosen, args.block)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         y = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
-        chosen = moe.choose_path(layers[0], b, cfg.top_k) if path == "auto" else path
-        h = torch.empty((b, cfg.top_k + cfg.num_shared, cfg.inter),
+        h = torch.empty((b, slots, cfg.inter),
                         dtype=torch.float32 if h_dtype == "f32" else torch.bfloat16, device=dev)
         variant = "expert" if b >= 4 else "token"
-        dws = torch.empty(max(16, (cfg.top_k + cfg.num_shared) * b * cfg.hidden * 4),
-                          dtype=torch.uint8, device=dev)
+        dws = torch.empty(max(16, slots * b * cfg.hidden * 4), dtype=torch.uint8, device=dev)
 
         def step(i, ev=None):
             L = layers[i % n_layers]
@@ -186,13 +264,18 @@ def main():
                 moe.layer(L, d["x"], d["ids"], d["wts"], path="grouped", block=args.block, y=y,
                           workspace=ws)
 
-        if chosen == "decode":
-            # the timed kernel sequence is exactly moe_layer's decode path
-            step(0)
-            y_ref, _ = moe.layer(layers[0], ins[0]["x"], ins[0]["ids"], ins[0]["wts"], path="decode")
-            torch.cuda.synchronize()
-            if not torch.equal(y, y_ref):
-                raise RuntimeError("timed decode sequence differs from moe_layer(decode)")
+        # verify, then benchmark: the timed kernel sequence is exactly
+        # moe_layer's, and its output matches the oracle on every checked token
+        step(0)
+        y_ref, got = moe.layer(layers[0], ins[0]["x"], ins[0]["ids"], ins[0]["wts"], path=chosen,
+                               block=args.block)
+        torch.cuda.synchronize()
+        if got != chosen or not torch.equal(y, y_ref):
+            raise RuntimeError("timed step sequence differs from moe_layer")
+        x_np, ids_np, w_np = ins[0]["np"]
+        par = parity(oracle, x_np, ids_np, w_np, sample_rows(b, n_check), y_ref, chosen)
+        if not par["pass"]:
+            raise RuntimeError(f"parity check failed before timing: {par}")
 
         for i in range(warmup):
             step(i)
@@ -223,14 +306,25 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         total_ms = s0.elapsed_time(s1)
-        del g
         if not torch.equal(y, y_eager):
             raise RuntimeError("graph replay differs from the eager steps")
+        # spread: further replays of the same graph, each timed alone
+        per = []
+        for _ in range(replays):
+            s0.record(stream)
+            g.replay()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            per.append(s0.elapsed_time(s1) * 1e3 / steps)
+        del g
         tot_bytes = sum(ins[i % n_layers]["bytes"] for i in range(steps))
         res = {"B": b, "path": chosen, "us_per_layer": total_ms * 1e3 / steps,
                "eager_us_per_layer": eager_ms * 1e3 / steps,
+               "replays_us": spread(per),
                "TBps": tot_bytes / (total_ms * 1e-3) / 1e12,
-               "U_mean": float(np.mean([d["U"] for d in ins])), "wall_s": wall}
+               "U_mean": float(np.mean([d["U"] for d in ins])), "wall_s": wall, "parity": par}
+        if copy_peak:
+            res["frac_of_copy_peak"] = res["TBps"] / copy_peak
         if chosen == "decode":
             gu = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
             dn = [evs[i][1].elapsed_time(evs[i][2]) for i in range(steps)]
@@ -239,17 +333,19 @@ def main():
             res["down_us"] = float(np.mean(dn)) * 1e3
             res["gate_up_GBps"] = gub / (sum(gu) * 1e-3) / 1e9
             res["gate_up_bytes_per_launch"] = gub / steps
+        log(f"{cfg.name} B={b} {chosen}: {res['us_per_layer']:.1f} us, {res['TBps']:.3f} TB/s, "
+            f"parity {par}")
         return res
 
-    main_res = run_steps(B, args.steps, args.warmup, args.path)
+    main_res = run_steps(B, args.steps, args.warmup, args.path, n_check=None)
 
     sweep = []
-    if not args.no_sweep and cfg is W.QWEN3_DECODE_MXFP8:
+    if not args.no_sweep and not args.headline_only and cfg is W.QWEN3_DECODE_MXFP8:
         for b in cfg.batches:
-            r = run_steps(b, 50, 5, args.path)
-            sweep.append({k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()
-                          if k in ("B", "path", "us_per_layer", "eager_us_per_layer", "TBps",
-                                   "U_mean", "gate_up_us", "down_us")})
+            r = run_steps(b, 50, 5, args.path, n_check=None)
+            sweep.append(rounded(r, ("B", "path", "us_per_layer", "eager_us_per_layer", "replays_us",
+                                     "TBps", "frac_of_copy_peak", "U_mean", "gate_up_us",
+                                     "down_us", "parity")))
 
     roofline = None
     if main_res["path"] == "decode":
@@ -262,38 +358,45 @@ def main():
                     "avg_launch_us": round(main_res["gate_up_us"], 2)}
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, B, arrays)
-    del layers, arrays, w0
+    if not args.no_cpu_baseline and not args.headline_only:
+        cpu = cpu_baseline(cfg, B, oracle)
+    del layers, w0
     torch.cuda.empty_cache()
 
-    router = [router_report(moe, W, torch, dev, stream, c, t)
-              for c, t in ((W.QWEN3_DECODE_MXFP8, B), (W.DEEPSEEK_V3_FP8_BLK128, 64),
-                           (W.PREFILL_ZIPF_MXFP8, 16384))]
+    accuracy = []
+    if not args.no_accuracy and not args.headline_only:
+        accuracy.append(accuracy_report(ctx, cfg, arrays, oracle, 32))
+    del arrays, oracle
 
-    grouped = []
-    if not args.no_grouped:
-        # DeepSeek-V3-shaped layer at B = 256 (HBM-bound; 32-row blocks,
-        # the fastest measured for a dozen tokens per expert) and the Zipf
-        # prefill step (MFMA-bound, 128-row blocks)
+    router, grouped, layers_sweep = [], [], []
+    if not args.headline_only:
+        router = [router_report(ctx, c, t)
+                  for c, t in ((W.QWEN3_DECODE_MXFP8, B), (W.DEEPSEEK_V3_FP8_BLK128, 64),
+                               (W.PREFILL_ZIPF_MXFP8, 16384))]
+    if not args.no_sweep and not args.headline_only:
+        # the metric's B = 1-256 over the other workloads: every batch is
+        # verified, then timed, on the path moe_layer picks and (where both
+        # run) on the other path too
+        for c, batches, kinds, n_check in (
+                (W.QWEN3_DECODE_MXFP8, (64, 128, 256), (None,), 4),
+                (W.DEEPSEEK_V3_FP8_BLK128, (1, 16, 64, 256), (None,), 2),
+                (W.MXFP4_SWEEP, (1, 2, 8, 32, 64, 128, 256), ("uniform", "zipf"), 3)):
+            layers_sweep += layer_sweep(ctx, c, batches, kinds, n_check,
+                                        accuracy if (c is W.MXFP4_SWEEP and not args.no_accuracy)
+                                        else None)
+            torch.cuda.empty_cache()
+    if not args.no_grouped and not args.headline_only:
+        # DeepSeek-V3-shaped layer at B = 256 (HBM-bound; 32-row blocks, the
+        # fastest measured for a dozen tokens per expert) and the Zipf prefill
+        # step (MFMA-bound, 128-row blocks)
         for c, t, bs, kind in ((W.DEEPSEEK_V3_FP8_BLK128, 256, 32, None),
                                (W.PREFILL_ZIPF_MXFP8, 16384, 128, "zipf")):
-            grouped.append(grouped_report(moe, W, torch, dev, stream, c, t, bs, kind,
-                                          steps=min(args.steps, 20)))
-            torch.cuda.empty_cache()
-
-    crossover = []
-    if args.crossover:
-        for c, batches in ((W.MXFP4_SWEEP, None),
-                           (W.QWEN3_DECODE_MXFP8, (1, 4, 8, 16, 32, 64, 128, 256)),
-                           (W.DEEPSEEK_V3_FP8_BLK128, (1, 8, 16, 32, 64, 128, 224))):
-            crossover += crossover_sweep(moe, W, torch, dev, stream, c, batches=batches,
-                                         kinds=("uniform", "zipf") if c is W.MXFP4_SWEEP else (None,))
+            grouped.append(grouped_report(ctx, c, t, bs, kind, steps=min(args.steps, 20)))
             torch.cuda.empty_cache()
 
     value = main_res["TBps"]
     out = {
-        "metric": "us per MoE layer & achieved HBM TB/s (fraction of peak), 1 GPU",
+        "metric": METRIC,
         "value": round(value, 4),
         "unit": "TB/s",
         "n_gpus": 1,
@@ -302,6 +405,7 @@ def main():
         "ms_per_step": round(main_res["us_per_layer"] / 1e3, 5),
         "us_per_layer": round(main_res["us_per_layer"], 2),
         "eager_us_per_layer": round(main_res["eager_us_per_layer"], 2),
+        "replays_us": main_res["replays_us"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -314,33 +418,184 @@ def main():
                    "experts": cfg.num_experts, "top_k": cfg.top_k, "batch": B,
                    "weight_format": cfg.fmt, "path": main_res["path"],
                    "layers_rotated": n_layers, "touched_experts_mean": main_res["U_mean"]},
+        "parity": main_res["parity"],
         "copy_peak_TBps": None if copy_peak is None else round(copy_peak, 3),
         "read_peak_TBps": None if read_peak is None else round(read_peak, 3),
         "frac_of_copy_peak": None if copy_peak is None else round(value / copy_peak, 4),
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(main_res[k], 2) for k in ("gate_up_us", "down_us") if k in main_res},
         "sweep": sweep,
+        "layers": layers_sweep,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "accuracy": accuracy,
         "router": router,
         "grouped": grouped,
     }
-    if crossover:
-        out["crossover"] = crossover
     print(json.dumps(out), flush=True)
 
 
-def _device_inputs(torch, dev, W, cfg, t, kind, variant=0):
+# ---------------------------------------------------------------------------
+
+def rounded(r, keys):
+    return {k: (round(r[k], 4) if isinstance(r[k], float) else r[k]) for k in keys if k in r}
+
+
+def down_expert_bytes(W, c):
+    shapes = W.weight_shapes(c)
+    tot = 0
+    for k in ("w2", "w2_scale"):
+        if k in shapes:
+            s, d = shapes[k]
+            tot += int(np.prod(s[1:])) * np.dtype(d).itemsize
+    return tot
+
+
+def to_dev_x(torch, dev, cfg, x):
+    return (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
+            else torch.from_numpy(x)).to(dev)
+
+
+def _device_inputs(ctx, cfg, t, kind, variant=0):
+    torch, W, dev = ctx["torch"], ctx["W"], ctx["dev"]
     x = W.activations(cfg, t, variant)
     ids, wts = W.routing(cfg, t, kind=kind, variant=variant)
-    xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.act == "bf16"
-          else torch.from_numpy(x)).to(dev)
-    return xd, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), ids
+    return dict(x=to_dev_x(torch, dev, cfg, x), ids=torch.from_numpy(ids).to(dev),
+                wts=torch.from_numpy(wts).to(dev), np=(x, ids, wts),
+                U=len(W.touched_experts(cfg, ids)))
 
 
-def router_report(moe, W, torch, dev, stream, cfg, t, steps=50):
+def layer_sweep(ctx, cfg, batches, kinds, n_check, accuracy=None, steps=10, replays=5, warmup=3):
+    """Whole-layer time over a batch list and routing kinds, on the path
+    moe_layer(AUTO) picks and on the other path where it runs: each case is
+    verified against the oracle first, then its steps (four routing draws
+    cycled) are captured in a HIP graph and replayed `replays` times."""
+    moe, W, torch, dev, stream = ctx["moe"], ctx["W"], ctx["torch"], ctx["dev"], ctx["stream"]
+    arrays = W.all_experts(cfg)
+    oracle = Oracle(cfg, arrays)
+    Wd = moe.Weights.from_arrays(cfg, arrays)
+    del arrays
+    ebytes = W.expert_bytes(cfg)
+    act = 2 if cfg.act == "bf16" else 4
+    out = []
+    for kind in kinds:
+        for t in batches:
+            ins = [_device_inputs(ctx, cfg, t, kind, v) for v in range(4)]
+            auto = moe.choose_path(Wd, t, cfg.top_k)
+            nbytes = float(np.mean([d["U"] * ebytes + t * cfg.hidden * act + t * cfg.top_k * 8
+                                    + t * cfg.hidden * 4 for d in ins]))
+            row = {"workload": cfg.name, "routing": kind or cfg.routing, "B": t,
+                   "entries": t * (cfg.top_k + cfg.num_shared), "auto": auto,
+                   "touched_mean": float(np.mean([d["U"] for d in ins])),
+                   "algorithmic_MB": round(nbytes / 1e6, 2)}
+            for path in ("decode", "grouped"):
+                need = moe.layer_workspace_bytes(Wd, t, cfg.top_k, path, 0)
+                y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+                try:
+                    moe.layer(Wd, ins[0]["x"], ins[0]["ids"], ins[0]["wts"], path=path, y=y,
+                              workspace=ws)
+                except moe.MoeError as err:
+                    if err.status != moe.ERR_UNSUPPORTED:
+                        raise
+                    continue            # this path does not run at this size
+                torch.cuda.synchronize()
+                x_np, ids_np, w_np = ins[0]["np"]
+                par = parity(oracle, x_np, ids_np, w_np, sample_rows(t, n_check if t > 8 else None),
+                             y, path)
+                if not par["pass"]:
+                    raise RuntimeError(f"parity check failed before timing: {row} {path} {par}")
+                for i in range(warmup):
+                    d = ins[i % 4]
+                    moe.layer(Wd, d["x"], d["ids"], d["wts"], path=path, y=y, workspace=ws)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(steps):
+                        d = ins[i % 4]
+                        moe.layer(Wd, d["x"], d["ids"], d["wts"], path=path, y=y, workspace=ws)
+                torch.cuda.synchronize()
+                per = []
+                for _ in range(replays):
+                    s0 = torch.cuda.Event(enable_timing=True)
+                    s1 = torch.cuda.Event(enable_timing=True)
+                    s0.record(stream)
+                    g.replay()
+                    s1.record(stream)
+                    torch.cuda.synchronize()
+                    per.append(s0.elapsed_time(s1) * 1e3 / steps)
+                del g
+                us = float(np.median(per))
+                entry = {"us": spread(per), "TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+                         "parity": par}
+                if ctx["copy_peak"]:
+                    entry["frac_of_copy_peak"] = round(nbytes / (us * 1e-6) / 1e12 / ctx["copy_peak"], 4)
+                if path == "grouped":
+                    fl = 6.0 * cfg.hidden * cfg.inter * t * (cfg.top_k + cfg.num_shared)
+                    entry["mfma_frac_useful"] = round(fl / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["fp8"], 4)
+                row[path] = entry
+            log(f"layer {row}")
+            out.append(row)
+            if accuracy is not None and t == 32:
+                accuracy.append(accuracy_report(ctx, cfg, None, oracle, t, kind=kind, Wd=Wd))
+    del Wd
+    return out
+
+
+def accuracy_report(ctx, cfg, arrays, oracle, t, kind=None, Wd=None):
+    """The two regimes on the same inputs against exact activations (oracle
+    mode none): the output-centric path keeps activations exact, the
+    expert-centric one quantises x and h to MXFP8 and holds slots in BF16
+    (the warp-decode post's accuracy section compares the two).  The grouped
+    path's h is requantised with two terms; the single-term reading is
+    measured too, by running the same kernels with the second term's codes
+    set to zero (a zero code contributes nothing whatever its scale)."""
+    moe, torch = ctx["moe"], ctx["torch"]
+    if Wd is None:
+        Wd = moe.Weights.from_arrays(cfg, arrays)
+    d = _device_inputs(ctx, cfg, t, kind)
+    x_np, ids_np, w_np = d["np"]
+    y_dec, _ = moe.layer(Wd, d["x"], d["ids"], d["wts"], path="decode")
+    y_grp, _ = moe.layer(Wd, d["x"], d["ids"], d["wts"], path="grouped")
+    y_one = grouped_single_term(ctx, Wd, cfg, d, t)
+    torch.cuda.synchronize()
+    exact = oracle.layer(x_np, ids_np, w_np, "none")
+    single = oracle.layer(x_np, ids_np, w_np, "mxfp8_single")
+    f = lambda y: y.double().cpu().numpy()
+    m_dec, m_grp, m_one = metrics(f(y_dec), exact), metrics(f(y_grp), exact), metrics(f(y_one), exact)
+    m_one_own = metrics(f(y_one), single)
+    res = {"workload": cfg.name, "routing": kind or cfg.routing, "B": t,
+           "decode_vs_exact": {k: float(f"{v:.4e}") for k, v in m_dec.items()},
+           "grouped_two_term_vs_exact": {k: float(f"{v:.4e}") for k, v in m_grp.items()},
+           "grouped_single_term_vs_exact": {k: float(f"{v:.4e}") for k, v in m_one.items()},
+           "grouped_single_term_vs_its_oracle_mode": {k: float(f"{v:.4e}") for k, v in m_one_own.items()},
+           "rel_l2_ratio_grouped_two_term_over_decode": round(m_grp["rel_l2"] / m_dec["rel_l2"], 2),
+           "rel_l2_ratio_grouped_single_term_over_decode": round(m_one["rel_l2"] / m_dec["rel_l2"], 2)}
+    log(f"accuracy {res}")
+    return res
+
+
+def grouped_single_term(ctx, Wd, cfg, d, t, bs=32):
+    """The grouped path's kernels with h's second term zeroed between the two
+    GEMMs: the single-requantisation pipeline."""
+    moe, torch = ctx["moe"], ctx["torch"]
+    k, S = cfg.top_k, cfg.num_shared
+    srt = moe.align_sort(d["ids"], cfg.num_experts, S, bs)
+    cap = srt["capacity"]
+    xq, xs = moe.gather_quant(d["x"], k + S, srt["sorted_token_ids"], srt["num_tokens_post_padded"],
+                              cap)
+    hq, hs = moe.grouped_gate_up(Wd, xq, xs, srt["expert_ids"], srt["num_tokens_post_padded"], cap,
+                                 bs)
+    hq[1].zero_()
+    so = moe.grouped_down(Wd, hq, hs, srt["sorted_token_ids"], srt["expert_ids"],
+                          srt["num_tokens_post_padded"], cap, bs, d["wts"], t, k)
+    return moe.combine(so, t, k + S)
+
+
+def router_report(ctx, cfg, t, steps=50):
     """Router front-end (gating scores -> top-k ids and weights) timed with
     HIP events; bytes = scores read + ids and weights written."""
+    moe, W, torch, dev, stream = ctx["moe"], ctx["W"], ctx["torch"], ctx["dev"], ctx["stream"]
     scores, bias = W.gating_scores(cfg, t)
     s = torch.from_numpy(scores).to(dev)
     b = None if bias is None else torch.from_numpy(bias).to(dev)
@@ -369,20 +624,25 @@ def router_report(moe, W, torch, dev, stream, cfg, t, steps=50):
             "biased": bias is not None, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
 
 
-def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmup=3):
-    """Expert-centric path on one layer: the five calls moe_layer makes
-    (align-sort, gather + MXFP8 quantisation, gate_up GEMM, down GEMM,
-    combine), each bracketed by HIP events on the launch stream.  MFMA
-    utilisation counts useful FLOPs only (padding rows excluded)."""
+def grouped_report(ctx, cfg, t, bs, kind, steps=20, warmup=3, n_check=4):
+    """Expert-centric path on one layer: the calls moe_layer makes, each
+    bracketed by HIP events on the launch stream, after a check of sampled
+    tokens against the oracle.  MFMA utilisation counts useful FLOPs only
+    (padding rows excluded)."""
+    moe, W, torch, dev, stream = ctx["moe"], ctx["W"], ctx["torch"], ctx["dev"], ctx["stream"]
     arrays = W.all_experts(cfg)
+    oracle = Oracle(cfg, arrays)
     Wd = moe.Weights.from_arrays(cfg, arrays)
     del arrays
-    x, ids, wts, ids_np = _device_inputs(torch, dev, W, cfg, t, kind)
+    d = _device_inputs(ctx, cfg, t, kind)
+    x, ids, wts = d["x"], d["ids"], d["wts"]
+    x_np, ids_np, w_np = d["np"]
     k, S = cfg.top_k, cfg.num_shared
     slots = k + S
     y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
     slot_out = torch.empty((t * slots, cfg.hidden), dtype=torch.bfloat16, device=dev)
     cap = moe.align_sort_capacity(t, k, cfg.num_experts, S, bs)
+    names = ["align_sort", "gather_quant", "gate_up_gemm", "down_gemm", "combine"]
 
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
@@ -406,17 +666,21 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
     torch.cuda.synchronize()
     if not torch.equal(y, y_ref):
         raise RuntimeError("timed grouped sequence differs from moe_layer(grouped)")
+    par = parity(oracle, x_np, ids_np, w_np, sample_rows(t, n_check), y_ref, "grouped")
+    if not par["pass"]:
+        raise RuntimeError(f"parity check failed before timing: {cfg.name} {par}")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    names = ["align_sort", "gather_quant", "gate_up_gemm", "down_gemm", "combine"]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
            for j, n in enumerate(names)}
-    total = float(np.mean([e[0].elapsed_time(e[5]) for e in evs])) * 1e3
+    totals = [e[0].elapsed_time(e[-1]) * 1e3 for e in evs]
+    total = float(np.mean(totals))
     entries = t * slots
     fl_gu = 2.0 * entries * cfg.hidden * 2 * cfg.inter
     fl_dn = 2.0 * entries * cfg.inter * cfg.hidden
@@ -427,7 +691,7 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
     io = t * cfg.hidden * act + ids_np.nbytes * 2 + t * cfg.hidden * 4
     res = {"workload": cfg.name, "tokens": t, "block": bs, "routing": kind or cfg.routing,
            "touched_experts": u, "capacity": cap,
-           "us_per_layer": round(total, 2),
+           "us_per_layer": round(total, 2), "us_spread": spread(totals),
            "kernels_us": {n: round(v, 2) for n, v in per.items()},
            "useful_TFLOP": round((fl_gu + fl_dn) / 1e12, 4),
            "gate_up_TFLOPs": round(fl_gu / (per["gate_up_gemm"] * 1e-6) / 1e12, 1),
@@ -437,67 +701,24 @@ def grouped_report(moe, W, torch, dev, stream, cfg, t, bs, kind, steps=20, warmu
            "mfma_frac_gate_up": round(fl_gu / (per["gate_up_gemm"] * 1e-6) / 1e12 / peak, 4),
            "mfma_frac_down": round(fl_dn / (per["down_gemm"] * 1e-6) / 1e12 / peak, 4),
            "mfma_frac_layer": round((fl_gu + fl_dn) / (total * 1e-6) / 1e12 / peak, 4),
-           "algorithmic_TBps": round((wbytes + io) / (total * 1e-6) / 1e12, 3)}
-    print(f"[bench] grouped {cfg.name} T={t} bs={bs}: {total:.1f} us "
-          f"(gate_up {per['gate_up_gemm']:.1f}, down {per['down_gemm']:.1f})",
-          file=sys.stderr, flush=True)
+           "algorithmic_TBps": round((wbytes + io) / (total * 1e-6) / 1e12, 3),
+           "parity": par}
+    log(f"grouped {cfg.name} T={t} bs={bs}: {total:.1f} us (gate_up {per['gate_up_gemm']:.1f}, "
+        f"down {per['down_gemm']:.1f}) parity {par}")
     del Wd
     return res
 
 
-def crossover_sweep(moe, W, torch, dev, stream, cfg, batches=None, kinds=(None,), steps=20,
-                    warmup=3, bs=32):
-    """Whole-layer time of both paths over a batch list (the configuration's
-    own by default) and routing kinds (None: the configuration's own), on one
-    layer's weights with several routing draws cycled."""
-    arrays = W.all_experts(cfg)
-    Wd = moe.Weights.from_arrays(cfg, arrays)
-    del arrays
-    out = []
-    for kind in kinds:
-        for t in batches or cfg.batches:
-            ins = [_device_inputs(torch, dev, W, cfg, t, kind, v) for v in range(4)]
-            row = {"workload": cfg.name, "routing": kind or cfg.routing, "B": t,
-                   "entries": t * (cfg.top_k + cfg.num_shared),
-                   "auto": moe.choose_path(Wd, t, cfg.top_k),
-                   "touched_mean": float(np.mean([len(W.touched_experts(cfg, i[3])) for i in ins]))}
-            for path in ("decode", "grouped"):
-                if path == "decode" and t * (cfg.top_k + cfg.num_shared) > 2048:
-                    continue
-                need = moe.layer_workspace_bytes(Wd, t, cfg.top_k, path, bs)
-                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-                y = torch.empty((t, cfg.hidden), dtype=torch.float32, device=dev)
-                for i in range(warmup):
-                    xd, idd, wd, _ = ins[i % 4]
-                    moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
-                torch.cuda.synchronize()
-                # the steps replayed from one HIP graph, as in the headline
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(steps):
-                        xd, idd, wd, _ = ins[i % 4]
-                        moe.layer(Wd, xd, idd, wd, path=path, block=bs, y=y, workspace=ws)
-                torch.cuda.synchronize()
-                s0 = torch.cuda.Event(enable_timing=True)
-                s1 = torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
-                g.replay()
-                s1.record(stream)
-                torch.cuda.synchronize()
-                del g
-                row[path + "_us"] = round(s0.elapsed_time(s1) * 1e3 / steps, 2)
-            print(f"[bench] crossover {row}", file=sys.stderr, flush=True)
-            out.append(row)
-    del Wd
-    return out
-
-
-def cpu_baseline(cfg, B, arrays, budget_s=12.0, max_calls=8):
+def cpu_baseline(cfg, B, oracle, budget_s=12.0, max_calls=8):
     """The float64 oracle timed on this host's cores on whole layer calls of
     the same workload (B tokens; successive routing draws) until about
-    `budget_s` seconds of CPU work have run (at most `max_calls` calls)."""
+    `budget_s` seconds of CPU work have run (at most `max_calls` calls).
+    Each call dequantises the experts it touches (stored format -> float64),
+    as the oracle does, without reusing the parity checks' cache."""
     import workloads as W
     from oracle import layer as L
+
+    arrays = oracle.arrays
 
     def get(e):
         return {k: (None if v is None else v[e]) for k, v in arrays.items()}

@@ -69,16 +69,29 @@ def _lut_e4m3():
     return F.decode_e4m3fn(np.arange(256, dtype=np.uint8))
 
 
+# Lookup tables of the exact decoders (formats.decode_*), indexed by the stored
+# byte: one E4M3 value, one E8M0 scale, or the two E2M1 values of a packed byte
+# (even element from the low nibble).
 _E4M3 = _lut_e4m3()
 _E8M0 = F.decode_e8m0(np.arange(256, dtype=np.uint8))
+_E2M1_PAIR = F.decode_e2m1(F.unpack_fp4(np.arange(256, dtype=np.uint8)[:, None]))
 
 
 def _mx(codes, scales, elem):
+    codes = np.asarray(codes)
     if elem == "e4m3":
-        v = _E4M3[np.asarray(codes)]
+        v = _E4M3[codes]
     else:
-        v = F.decode_e2m1(F.unpack_fp4(codes))
+        v = _E2M1_PAIR[codes].reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
     s = np.repeat(_E8M0[np.asarray(scales)], F.MX_BLOCK, axis=-1)[..., : v.shape[-1]]
+    return v * s
+
+
+def _blk128(codes, scales):
+    v = _E4M3[np.asarray(codes)]
+    r, k = v.shape[-2], v.shape[-1]
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    s = np.repeat(np.repeat(s, 128, axis=-2), 128, axis=-1)[..., :r, :k]
     return v * s
 
 
@@ -87,18 +100,24 @@ def dequant_expert(fmt, raw):
 
     raw: dict with "w13" [2][I][H*], "w2" [H][I*] and, per format,
     "w13_scale"/"w2_scale" (MX: E8M0 bytes per 32 along K; fp8_blk128: float32
-    per 128x128 tile of each [out][in] matrix).
+    per 128x128 tile of each [out][in] matrix; "f64": float64 values, taken
+    as they are).
     """
     if fmt == "f32":
         w13 = np.asarray(raw["w13"], dtype=np.float32).astype(np.float64)
         w2 = np.asarray(raw["w2"], dtype=np.float32).astype(np.float64)
+    elif fmt == "f64":
+        # values already dequantised (for callers that reuse one expert's
+        # dequantised weights across several evaluations)
+        w13 = np.asarray(raw["w13"], dtype=np.float64)
+        w2 = np.asarray(raw["w2"], dtype=np.float64)
     elif fmt in ("mxfp8", "mxfp4"):
         elem = "e4m3" if fmt == "mxfp8" else "e2m1"
         w13 = _mx(raw["w13"], raw["w13_scale"], elem)
         w2 = _mx(raw["w2"], raw["w2_scale"], elem)
     elif fmt == "fp8_blk128":
-        w13 = F.dequant_blk128(raw["w13"], raw["w13_scale"])
-        w2 = F.dequant_blk128(raw["w2"], raw["w2_scale"])
+        w13 = _blk128(raw["w13"], raw["w13_scale"])
+        w2 = _blk128(raw["w2"], raw["w2_scale"])
     else:
         raise ValueError(fmt)
     return w13[0], w13[1], w2

@@ -232,3 +232,20 @@ def test_mxfp8_modes_are_the_documented_steps_of_each_other():
     e1 = np.linalg.norm(y1 - exact_h) / np.linalg.norm(exact_h)
     e2 = np.linalg.norm(y2 - exact_h) / np.linalg.norm(exact_h)
     assert e2 < e1 / 4, (e1, e2)
+
+
+def test_f64_weights_are_taken_as_given():
+    """fmt "f64" hands over dequantised weights: the layer equals the one run
+    on the stored format."""
+    cfg = TINY["fp8_blk128"]
+    x, ids, w = _inputs(cfg, 3)
+    get = _getter(cfg)
+
+    def get64(e):
+        wg, wu, wd = L.dequant_expert(cfg.fmt, get(e))
+        return {"w13": np.stack([wg, wu]), "w2": wd}
+    for mode in L.MODES:
+        y = L.moe_layer(x, ids, w, act_quant=mode, **_kw(cfg, getter=get))
+        y64 = L.moe_layer(x, ids, w, act_quant=mode, fmt="f64", num_experts=cfg.num_experts,
+                          num_shared=cfg.num_shared, get_expert=get64)
+        assert np.array_equal(y, y64)
