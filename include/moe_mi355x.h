@@ -333,6 +333,29 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
                      void* workspace, size_t workspace_bytes,
                      int32_t* chosen, void* stream);
 
+/*
+ * moe_layer_noalloc: moe_layer with no caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a device array
+ * inside the library, moe_layer_noalloc_max_bytes() bytes (32 MiB), one copy
+ * per GPU, held from the library's load until the process ends.  Nothing is
+ * allocated or freed by the call; the caller still owns x, the routing and y.
+ *   Arguments and results as moe_layer.
+ *   MOE_ERR_WORKSPACE_TOO_SMALL (nothing enqueued) when
+ *   moe_layer_workspace_bytes(W, T, k, path, block_size) exceeds the array,
+ *   e.g. the grouped path at prefill sizes.
+ * All calls on one GPU share its array and leave their contents in it (no
+ * step of the layer needs it cleared): calls that overlap on one GPU --
+ * different streams, or threads enqueueing at the same time -- race and must
+ * be serialised by the caller.
+ */
+size_t moe_layer_noalloc_max_bytes(void);
+
+moe_status moe_layer_noalloc(const moe_weights* W, const void* x, int32_t x_dtype,
+                             const int32_t* topk_ids, const float* topk_weights,
+                             int32_t T, int32_t k, void* y, int32_t y_dtype,
+                             int32_t path, int32_t block_size, int32_t* chosen, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,9 @@ _SIGS = {
     "moe_layer_workspace_bytes": (_Z, [_WP, _I, _I, _I, _I]),
     "moe_layer": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _Z,
                        ctypes.POINTER(_I), _P]),
+    "moe_layer_noalloc_max_bytes": (_Z, []),
+    "moe_layer_noalloc": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I,
+                               ctypes.POINTER(_I), _P]),
     "moe_util_copy": (_I, [_P, _P, _Z, _P]),
     "moe_util_read": (_I, [_P, _Z, _P, _P]),
     "moe_util_read_sink_len": (_I, []),
@@ -330,6 +333,25 @@ def layer(W, x, topk_ids, topk_weights, path="auto", block=0, y=None, y_dtype="f
                         _stream(stream))
     _check(st, "moe_layer")
     return y, PATH_NAME.get(chosen.value, "?")
+
+
+def layer_noalloc_max_bytes():
+    load()
+    return _lib.moe_layer_noalloc_max_bytes()
+
+
+def layer_noalloc(W, x, topk_ids, topk_weights, y, path="auto", block=0, stream=None):
+    """moe_layer_noalloc: y [T][H] (caller-allocated, written in place) with
+    the library's own device array as workspace; nothing is allocated here.
+    Returns the path that ran."""
+    load()
+    t, k = topk_ids.shape
+    chosen = ctypes.c_int32(-1)
+    st = _lib.moe_layer_noalloc(W.ref, _ptr(x), _dt(x), _ptr(topk_ids), _ptr(topk_weights), t, k,
+                                _ptr(y), _dt(y), PATH[path], block, ctypes.byref(chosen),
+                                _stream(stream))
+    _check(st, "moe_layer_noalloc")
+    return PATH_NAME.get(chosen.value, "?")
 
 
 # ---- measurement kernels ------------------------------------------------

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include <atomic>
 #include <cmath>
 #include <algorithm>
 
@@ -163,6 +164,41 @@ size_t decode_h_bytes(const moe_weights* W, int32_t T, int32_t k) {
 
 size_t decode_workspace(const moe_weights* W, int32_t T, int32_t k) {
   return decode_h_bytes(W, T, k) + align_up((size_t)T * (k + W->num_shared) * W->hidden * 4);
+}
+
+// ---- workspace held by the library, for callers that cannot allocate -----
+
+constexpr size_t kScratchBytes = size_t(32) << 20;   // per device
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+}  // namespace
+
+// The workspace of moe_layer_noalloc: one copy per device, alive until the
+// process ends.  Host code never passes the symbol itself to a kernel (on the
+// host it only names the variable); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of the current device's copy of `scratch`, looked up on
+// that device's first call and kept.  Concurrent first calls look it up twice
+// and store the same address.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -419,6 +455,30 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
                                k, so, s);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(moe::launch_combine(so, MOE_DT_BF16, T, slots, W->hidden, y, y_dtype, s));
+}
+
+size_t moe_layer_noalloc_max_bytes(void) { return kScratchBytes; }
+
+moe_status moe_layer_noalloc(const moe_weights* W, const void* x, int32_t x_dtype,
+                             const int32_t* topk_ids, const float* topk_weights, int32_t T,
+                             int32_t k, void* y, int32_t y_dtype, int32_t path,
+                             int32_t block_size, int32_t* chosen, void* stream) {
+  moe_status st = check_weights(W);
+  if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_GROUPED)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0)
+    return moe_layer(W, x, x_dtype, topk_ids, topk_weights, T, k, y, y_dtype, path, block_size,
+                     nullptr, 0, chosen, stream);
+  // the whole workspace of this call must fit the library's array
+  if (moe_layer_workspace_bytes(W, T, k, path, block_size) > kScratchBytes)
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return from_hip(e);
+  return moe_layer(W, x, x_dtype, topk_ids, topk_weights, T, k, y, y_dtype, path, block_size, ws,
+                   kScratchBytes, chosen, stream);
 }
 
 // ---- measurement helpers -----------------------------------------------

@@ -201,3 +201,25 @@ def test_library_reads_no_tuning_environment(lib):
     import mixture_experts_decode_amd as moe
     blob = open(moe.LIB_PATH, "rb").read()
     assert b"MOE_TUNE" not in blob and b"getenv" not in blob
+
+
+def test_noalloc_entry_point_host_checks(lib):
+    """moe_layer_noalloc checks its arguments and the size of its array on
+    the host: on a GPU-less host these return before any device call."""
+    moe = __import__("mixture_experts_decode_amd")
+    P = ctypes.c_void_p
+    dummy = P(4096)
+    assert lib.moe_layer_noalloc_max_bytes() == 32 << 20
+    w = _weights(moe)
+    assert lib.moe_layer_noalloc(None, dummy, 1, dummy, dummy, 4, 8, dummy, 0, 0, 0, None,
+                                 None) == moe.ERR_INVALID_ARG
+    assert lib.moe_layer_noalloc(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 7, 0,
+                                 None, None) == moe.ERR_INVALID_ARG
+    # the grouped path at a prefill size needs far more than the array
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 16384, 8, 2, 128) > 32 << 20
+    assert lib.moe_layer_noalloc(ctypes.byref(w), dummy, 1, dummy, dummy, 16384, 8, dummy, 0, 2,
+                                 128, None, None) == moe.ERR_WORKSPACE_TOO_SMALL
+    chosen = ctypes.c_int32(-1)
+    assert lib.moe_layer_noalloc(ctypes.byref(w), None, 1, None, None, 0, 8, None, 0, 0, 0,
+                                 ctypes.byref(chosen), None) == moe.OK
+    assert chosen.value == 1
