@@ -14,10 +14,11 @@
  *    the expert weight rows it needs, converts the stored format in registers
  *    and keeps FP32 accumulators (warp-decode post: the two kernels, warp
  *    independence);
- *  - grouped (expert-centric, large batches): moe_align_sort, then
- *    moe_gather_quant, moe_grouped_gate_up, moe_grouped_down, moe_combine on
- *    gfx950 block-scaled matrix cores (align-and-sort article: background,
- *    D-C-P algorithm, CK fused-MoE section on online FP8 quantisation).
+ *  - grouped (expert-centric, large batches): moe_align_sort and
+ *    moe_quant_rows, then moe_grouped_gate_up, moe_grouped_down, moe_combine
+ *    on gfx950 block-scaled matrix cores (align-and-sort article: background,
+ *    D-C-P algorithm, CK fused-MoE section on online FP8 quantisation and on
+ *    the sort feeding the GEMM).
  *
  * moe_layer runs either regime, or picks one (moe_choose_path).
  *
@@ -205,33 +206,37 @@ moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k,
 /* ------------------------------------------------------------------ */
 
 /*
- * moe_gather_quant: for every sorted row r < *num_tokens_post_padded, reads
- * x row t = sorted_token_ids[r] / slots (zeros for a sentinel row) and
- * MX-quantises it per 32 consecutive elements: shared exponent
- * floor(log2 amax) - 8 (clamped to [-127, 127], -127 for a zero block), scale
- * byte = exponent + 127, elements divided by 2^exponent, saturated to +-448
- * and rounded to the nearest E4M3 value, ties to even (align-and-sort article,
- * CK section: online FP8 quantisation of tokens ahead of the grouped GEMM;
- * warp-decode post, buffer section: the expert-major activation copy).
+ * moe_quant_rows: MX-quantises each of the T rows of x once, per 32
+ * consecutive elements: shared exponent floor(log2 amax) - 8 (clamped to
+ * [-127, 127], -127 for a zero block), scale byte = exponent + 127, elements
+ * divided by 2^exponent, saturated to +-448 and rounded to the nearest E4M3
+ * value, ties to even (align-and-sort article, CK section: online FP8
+ * quantisation of the tokens ahead of the grouped GEMM).  A token is
+ * quantised once however many slots route it; moe_grouped_gate_up reads each
+ * sorted row's activations from its token's row, so no per-slot gathered copy
+ * exists (warp-decode post, buffer section: the expert-major activation copy
+ * is a cost of the expert-centric path).
  *   x    device [T][H], x_dtype (BF16 or F32)
- *   xq   device [capacity][H] E4M3 bytes;  xs device [capacity][H/32] E8M0
- * H must be a multiple of 32.
+ *   xq   device [T][H] E4M3 bytes;  xs device [T][H/32] E8M0 bytes
+ * H must be a multiple of 32 and T*H at most 2^31 - 1.
  */
-moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H,
-                            int32_t slots, const int32_t* sorted_token_ids,
-                            const int32_t* num_tokens_post_padded, int32_t capacity,
-                            uint8_t* xq, uint8_t* xs, void* stream);
+moe_status moe_quant_rows(const void* x, int32_t x_dtype, int32_t T, int32_t H, uint8_t* xq,
+                          uint8_t* xs, void* stream);
 
 /*
  * moe_grouped_gate_up: for every block b < *num_tokens_post_padded/block_size
- * with expert e = expert_ids[b], G = Xq[b] Wg[e]^T and U = Xq[b] Wu[e]^T on
- * block-scaled MFMA with FP32 accumulation, then h = SiLU(G) * U requantised
- * per 32 consecutive neurons as two MXFP8 terms, hi = Q(h) and
- * lo = Q(h - hi), with the rule of moe_gather_quant (GC-MoE abstract: grouped
- * GEMM with SwiGLU and requantisation fused in the epilogue).  The second
- * term absorbs the code flips a single requantisation would take from the
- * matrix core's accumulation error.
- *   xq/xs   device, from moe_gather_quant
+ * with expert e = expert_ids[b], G = A[b] Wg[e]^T and U = A[b] Wu[e]^T on
+ * block-scaled MFMA with FP32 accumulation, where row r of A[b] is token row
+ * sorted_token_ids[r] / slots of xq (the matrix-core loads follow the sort;
+ * a padding row reads token 0 and its results are never used), then
+ * h = SiLU(G) * U requantised per 32 consecutive neurons as two MXFP8 terms,
+ * hi = Q(h) and lo = Q(h - hi), with the rule of moe_quant_rows (GC-MoE
+ * abstract: grouped GEMM with SwiGLU and requantisation fused in the
+ * epilogue).  The second term absorbs the code flips a single requantisation
+ * would take from the matrix core's accumulation error.
+ *   xq/xs   device [T][H] and [T][H/32], from moe_quant_rows
+ *   T, k    tokens and routed slots of the sort (slots = k + num_shared)
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded: from moe_align_sort
  *   hq      device [2][capacity][I] E4M3 (hi rows, then lo rows)
  *   hs      device [2][capacity][I/32] E8M0
  * Weight formats: MOE_W_MXFP8, MOE_W_MXFP4, MOE_W_FP8_BLK128.
@@ -239,6 +244,7 @@ moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H
  * otherwise).
  */
 moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const uint8_t* xs,
+                               int32_t T, int32_t k, const int32_t* sorted_token_ids,
                                const int32_t* expert_ids,
                                const int32_t* num_tokens_post_padded, int32_t capacity,
                                int32_t block_size, uint8_t* hq, uint8_t* hs, void* stream);

@@ -54,8 +54,8 @@ _SIGS = {
     "moe_align_sort_capacity": (_Z, [_I, _I, _I, _I, _I]),
     "moe_align_sort_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_align_sort": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
-    "moe_gather_quant": (_I, [_P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
-    "moe_grouped_gate_up": (_I, [_WP, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "moe_quant_rows": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_grouped_gate_up": (_I, [_WP, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P]),
     "moe_grouped_down": (_I, [_WP, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _I, _P]),
     "moe_topk_route": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
@@ -237,24 +237,28 @@ def align_sort(topk_ids, num_experts, num_shared, block, stream=None):
 
 
 @_on_stream
-def gather_quant(x, slots, sorted_ids, npp, capacity, stream=None):
+def quant_rows(x, stream=None):
+    """Each token row of x [T][H] quantised once to MXFP8: (xq [T][H] u8,
+    xs [T][H/32] u8)."""
     load()
     t, h = x.shape
-    xq = torch.empty((capacity, h), dtype=torch.uint8, device=x.device)
-    xs = torch.empty((capacity, h // 32), dtype=torch.uint8, device=x.device)
-    st = _lib.moe_gather_quant(_ptr(x), _dt(x), t, h, slots, _ptr(sorted_ids), _ptr(npp), capacity,
-                               _ptr(xq), _ptr(xs), _stream(stream))
-    _check(st, "moe_gather_quant")
+    xq = torch.empty((t, h), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((t, h // 32), dtype=torch.uint8, device=x.device)
+    st = _lib.moe_quant_rows(_ptr(x), _dt(x), t, h, _ptr(xq), _ptr(xs), _stream(stream))
+    _check(st, "moe_quant_rows")
     return xq, xs
 
 
 @_on_stream
-def grouped_gate_up(W, xq, xs, expert_ids, npp, capacity, block, stream=None):
+def grouped_gate_up(W, xq, xs, t, k, sorted_ids, expert_ids, npp, capacity, block, stream=None):
+    """Grouped gate_up GEMM over the sorted rows; row r reads token row
+    sorted_ids[r] // (k + S) of xq / xs.  Returns (hq [2][cap][I], hs [2][cap][I/32])."""
     load()
     hq = torch.empty((2, capacity, W.inter), dtype=torch.uint8, device=xq.device)
     hs = torch.empty((2, capacity, W.inter // 32), dtype=torch.uint8, device=xq.device)
-    st = _lib.moe_grouped_gate_up(W.ref, _ptr(xq), _ptr(xs), _ptr(expert_ids), _ptr(npp), capacity,
-                                  block, _ptr(hq), _ptr(hs), _stream(stream))
+    st = _lib.moe_grouped_gate_up(W.ref, _ptr(xq), _ptr(xs), t, k, _ptr(sorted_ids),
+                                  _ptr(expert_ids), _ptr(npp), capacity, block, _ptr(hq), _ptr(hs),
+                                  _stream(stream))
     _check(st, "moe_grouped_gate_up")
     return hq, hs
 

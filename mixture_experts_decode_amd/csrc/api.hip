@@ -16,7 +16,7 @@ namespace {
 using moe::kDecodeMaxEntries;
 using moe::kMaxExpertsTotal;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -107,7 +107,7 @@ double expert_bytes(const moe_weights* W) {
 //           the smaller of the two showing through, plus 4 us;
 //  grouped: the same bytes at 5.2 TB/s (4.0 TB/s for E2M1 weights, whose
 //           stage rows are half cache lines) with the matrix work hidden,
-//           plus 25 us for sort, gather, combine and launches.
+//           plus 25 us for sort, quantisation, combine and launches.
 // The touched experts are their expectation under uniform routing; skewed
 // routing touches fewer, which favours the grouped path a little earlier
 // than this predicts.
@@ -142,8 +142,8 @@ GroupedLayout grouped_layout(const moe_weights* W, int32_t T, int32_t k, int32_t
   L.offsets = take((size_t)(n_exp + 1) * 4);
   L.npp = take(4);
   L.as_ws = take(moe::align_sort_workspace_bytes(n, n_exp));
-  L.xq = take((size_t)L.cap * W->hidden);
-  L.xs = take((size_t)L.cap * (W->hidden / 32));
+  L.xq = take((size_t)T * W->hidden);                // each token quantised once
+  L.xs = take((size_t)T * (W->hidden / 32));
   L.hq = take((size_t)2 * L.cap * W->inter);          // hi and lo terms
   L.hs = take((size_t)2 * L.cap * (W->inter / 32));
   L.slot_out = take((size_t)n * W->hidden * 2);      // BF16 slot outputs
@@ -302,35 +302,34 @@ moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
                                          as_stream(stream)));
 }
 
-moe_status moe_gather_quant(const void* x, int32_t x_dtype, int32_t T, int32_t H, int32_t slots,
-                            const int32_t* sorted_token_ids,
-                            const int32_t* num_tokens_post_padded, int32_t capacity, uint8_t* xq,
-                            uint8_t* xs, void* stream) {
-  if (!dtype_ok(x_dtype) || T < 0 || H <= 0 || slots < 1 || capacity < 0)
-    return MOE_ERR_INVALID_ARG;
+moe_status moe_quant_rows(const void* x, int32_t x_dtype, int32_t T, int32_t H, uint8_t* xq,
+                          uint8_t* xs, void* stream) {
+  if (!dtype_ok(x_dtype) || T < 0 || H <= 0) return MOE_ERR_INVALID_ARG;
   if (H % 32) return MOE_ERR_UNSUPPORTED;
-  if (capacity == 0) return MOE_OK;
-  if ((T > 0 && !x) || !sorted_token_ids || !num_tokens_post_padded || !xq || !xs)
-    return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_gather_quant(x, x_dtype, T, H, slots, sorted_token_ids,
-                                           num_tokens_post_padded, capacity, xq, xs,
-                                           as_stream(stream)));
+  if (T == 0) return MOE_OK;
+  if (!x || !xq || !xs) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * H > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_quant_rows(x, x_dtype, T, H, xq, xs, as_stream(stream)));
 }
 
 moe_status moe_grouped_gate_up(const moe_weights* W, const uint8_t* xq, const uint8_t* xs,
+                               int32_t T, int32_t k, const int32_t* sorted_token_ids,
                                const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                                int32_t capacity, int32_t block_size, uint8_t* hq, uint8_t* hs,
                                void* stream) {
   moe_status st = check_weights(W);
   if (st != MOE_OK) return st;
+  if ((st = check_routing(W, T, k)) != MOE_OK) return st;
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
   if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * W->hidden > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (capacity == 0) return MOE_OK;
-  if (!xq || !xs || !expert_ids || !num_tokens_post_padded || !hq || !hs)
+  if (capacity == 0 || T == 0) return MOE_OK;
+  if (!xq || !xs || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !hq || !hs)
     return MOE_ERR_INVALID_ARG;
-  return from_hip(moe::launch_grouped_gate_up(*W, xq, xs, expert_ids, num_tokens_post_padded,
-                                              capacity, block_size, hq, hs, as_stream(stream)));
+  return from_hip(moe::launch_grouped_gate_up(*W, xq, xs, T, k + W->num_shared, sorted_token_ids,
+                                              expert_ids, num_tokens_post_padded, capacity,
+                                              block_size, hq, hs, as_stream(stream)));
 }
 
 moe_status moe_grouped_down(const moe_weights* W, const uint8_t* hq, const uint8_t* hs,
@@ -431,6 +430,8 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   if (block_size == 0) block_size = auto_block(W, T, k);
   if (!grouped_supported(W) || !block_ok(block_size)) return MOE_ERR_UNSUPPORTED;
   if (W->hidden % 128 || W->inter % 128) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * W->hidden > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
   const GroupedLayout L = grouped_layout(W, T, k, block_size);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ERR_INVALID_ARG;
@@ -447,9 +448,10 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   hipError_t e = moe::launch_align_sort(topk_ids, T, k, W->num_experts, W->num_shared, block_size,
                                         sorted, eids, offs, npp, ws + L.as_ws, s);
   if (e != hipSuccess) return from_hip(e);
-  e = moe::launch_gather_quant(x, x_dtype, T, W->hidden, slots, sorted, npp, L.cap, xq, xs, s);
+  e = moe::launch_quant_rows(x, x_dtype, T, W->hidden, xq, xs, s);
   if (e != hipSuccess) return from_hip(e);
-  e = moe::launch_grouped_gate_up(*W, xq, xs, eids, npp, L.cap, block_size, hq, hs, s);
+  e = moe::launch_grouped_gate_up(*W, xq, xs, T, slots, sorted, eids, npp, L.cap, block_size, hq,
+                                  hs, s);
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_grouped_down(*W, hq, hs, sorted, eids, npp, L.cap, block_size, topk_weights, T,
                                k, so, s);

@@ -1,5 +1,7 @@
-// Expert-centric (grouped) path: gather + MXFP8 activation quantisation,
-// grouped gate_up / down GEMMs on gfx950 block-scaled MFMA, ordered combine.
+// Expert-centric (grouped) path: MXFP8 quantisation of each token row once,
+// grouped gate_up / down GEMMs on gfx950 block-scaled MFMA (the gate_up
+// GEMM's activation loads follow the align-sort order to the token rows),
+// ordered combine.
 
 #include "device.h"
 #include "internal.h"
@@ -52,25 +54,20 @@ __device__ __forceinline__ float pow2_neg(int e) {
 
 __device__ __forceinline__ float pow2(int e) { return pow2_neg(-e); }
 
-// One wavefront per sorted row; each lane quantises whole 32-element blocks.
+// One wavefront per token row; each lane quantises whole 32-element blocks.
+// Every token is quantised once, whatever number of slots routes it: the
+// gate_up GEMM reads a sorted row's activations from its token's row.
 template <bool XF32>
-__global__ __launch_bounds__(kGqBlock) void gather_quant_kernel(
-    const void* __restrict__ x, int H, int slots, int sentinel, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ npp, int capacity, uint8_t* __restrict__ xq,
-    uint8_t* __restrict__ xs) {
+__global__ __launch_bounds__(kGqBlock) void quant_rows_kernel(const void* __restrict__ x, int T,
+                                                              int H, uint8_t* __restrict__ xq,
+                                                              uint8_t* __restrict__ xs) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int r = blockIdx.x * (kGqBlock / kWave) + (threadIdx.x >> 6);
-  if (r >= capacity || r >= *npp) return;
-  const int ent = sorted[r];
-  const bool pad = ent < 0 || ent >= sentinel;
-  const int t = pad ? 0 : ent / slots;
+  const int t = blockIdx.x * (kGqBlock / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
   const int nblk = H >> 5;
   for (int b = lane; b < nblk; b += kWave) {
     float v[32];
-    if (pad) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
-    } else if constexpr (XF32) {
+    if constexpr (XF32) {
       const float* p = reinterpret_cast<const float*>(x) + (size_t)t * H + b * 32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -102,10 +99,10 @@ __global__ __launch_bounds__(kGqBlock) void gather_quant_kernel(
     for (int i = 0; i < 8; ++i)
       out[i >> 2][i & 3] = e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv,
                                   v[4 * i + 3] * inv);
-    uint8_t* dq = xq + (size_t)r * H + b * 32;
+    uint8_t* dq = xq + (size_t)t * H + b * 32;
     *reinterpret_cast<u32x4*>(dq) = out[0];
     *reinterpret_cast<u32x4*>(dq + 16) = out[1];
-    xs[(size_t)r * nblk + b] = (uint8_t)(e + 127);
+    xs[(size_t)t * nblk + b] = (uint8_t)(e + 127);
   }
 }
 
@@ -147,18 +144,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ s
 
 }  // namespace
 
-hipError_t launch_gather_quant(const void* x, int x_dtype, int T, int H, int slots,
-                               const int32_t* sorted, const int32_t* npp, int capacity,
-                               uint8_t* xq, uint8_t* xs, hipStream_t s) {
+hipError_t launch_quant_rows(const void* x, int x_dtype, int T, int H, uint8_t* xq, uint8_t* xs,
+                             hipStream_t s) {
+  if (T == 0) return hipSuccess;
   const int rows_per_block = kGqBlock / kWave;
-  const int blocks = (capacity + rows_per_block - 1) / rows_per_block;
-  const int sentinel = T * slots;
+  const int blocks = (T + rows_per_block - 1) / rows_per_block;
   if (x_dtype == MOE_DT_F32)
-    hipLaunchKernelGGL(gather_quant_kernel<true>, dim3(blocks), dim3(kGqBlock), 0, s, x, H, slots,
-                       sentinel, sorted, npp, capacity, xq, xs);
+    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(blocks), dim3(kGqBlock), 0, s, x, T, H, xq, xs);
   else
-    hipLaunchKernelGGL(gather_quant_kernel<false>, dim3(blocks), dim3(kGqBlock), 0, s, x, H,
-                       slots, sentinel, sorted, npp, capacity, xq, xs);
+    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(blocks), dim3(kGqBlock), 0, s, x, T, H, xq,
+                       xs);
   return hipGetLastError();
 }
 
@@ -184,7 +179,10 @@ hipError_t launch_combine(const void* slot_out, int slot_dtype, int T, int slots
 // grouped GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4
 //
 // A workgroup of 4 or 8 wavefronts computes a BM x BN tile: BM sorted rows (one
-// align-sort block, hence one expert) against BN weight rows.  Both operand
+// align-sort block, hence one expert) against BN weight rows.  In gate_up the
+// sorted rows' activations are the quantised rows of their tokens, fetched
+// through sorted_token_ids by the same direct-to-LDS loads (no gathered copy
+// exists); in down they are the sorted rows of h that gate_up wrote.  Both operand
 // tiles travel HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4),
 // in NS stages of 64 * KSTEPS K, so NS-1 stages are in flight while one is
 // consumed and no registers are spent on staging.  An LDS row holds one
@@ -210,15 +208,15 @@ constexpr int kLdsBytes = 160 * 1024;    // gfx950 LDS per workgroup
 constexpr int kGroupM = 4;               // M-blocks per raster group
 
 struct GemmArgs {
-  const uint8_t* a;        // activations [cap][K] E4M3 (down: the hi term of h)
-  const uint8_t* as;       // [cap][K/32] E8M0
+  const uint8_t* a;        // gate_up: token rows [T][K] E4M3; down: sorted rows of h's hi term [cap][K]
+  const uint8_t* as;       // [T or cap][K/32] E8M0
   const uint8_t* a_lo;     // down: lo term of h [cap][K]
   const uint8_t* as_lo;    // down: [cap][K/32]
   const uint8_t* b;        // expert weights, rows of K (E4M3 or packed E2M1)
   const void* bs;          // weight scales (E8M0 bytes or float 128x128 tiles)
   const int32_t* expert_ids;
   const int32_t* npp;
-  const int32_t* sorted;   // down: entry of each sorted row
+  const int32_t* sorted;   // entry of each sorted row (gate_up: its token row; down: its slot)
   const float* wts;        // down: routing weights
   uint8_t* hq;             // gate_up out [2][cap][I]: hi term, then lo term
   uint8_t* hs;             // gate_up out [2][cap][I/32]
@@ -372,6 +370,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
                             : r32 * S::BRB + (((4 * st + 2 * q + h) ^ swz<S::BP>(r32)) << 4);
     }
 
+  // token row of sorted row r (gate_up): the entry's token, or token 0 for
+  // a padding row
+  auto token_of = [&](int r) -> int {
+    const int ent = g.sorted[r];
+    return (unsigned)ent < (unsigned)g.sentinel ? ent / g.slots : 0;
+  };
+
   // per-tile state, set by setup(t) for the tile whose loads are queued
   constexpr int AR_I = 1024 / S::ARB, BR_I = 1024 / S::BRB;   // rows per DMA instruction
   int row0 = 0, nt = 0;
@@ -404,36 +409,43 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
 
     // ---- DMA sources: a uniform base per operand (advanced by the stage)
     // plus a 32-bit per-lane offset that stays fixed for the whole tile
-    a_base0 = g.a + (size_t)row0 * g.K;
+    // gate_up reads each sorted row's activations from its token's row
+    // (padding rows read token 0; their outputs are never used); down reads
+    // the sorted rows of h that gate_up wrote
+    a_base0 = GATEUP ? g.a : g.a + (size_t)row0 * g.K;
     a_base1 = TERMS > 1 ? g.a_lo + (size_t)row0 * g.K : a_base0;
     b_base = g.b + (size_t)e * g.rows_per_expert * g.b_row_bytes;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i) {
       const int j = (w + S::WAVES * i) % (BM / AR_I);
       const int row = AR_I * j + ln / S::AP;
-      a_src[i] = (uint32_t)(row * g.K + (((ln % S::AP) ^ swz<S::AP>(row)) << 4));
+      const uint32_t src_row = GATEUP ? (uint32_t)token_of(row0 + row) : (uint32_t)row;
+      a_src[i] = src_row * (uint32_t)g.K + (uint32_t)(((ln % S::AP) ^ swz<S::AP>(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i) {
       const int row = BR_I * (w + S::WAVES * i) + ln / S::BP;
       b_src[i] = (uint32_t)(b_row(nt, row) * g.b_row_bytes + (((ln % S::BP) ^ swz<S::BP>(row)) << 4));
     }
-    sa_base0 = g.as + (size_t)row0 * k_blocks;
+    sa_base0 = GATEUP ? g.as : g.as + (size_t)row0 * k_blocks;
     sa_base1 = TERMS > 1 ? g.as_lo + (size_t)row0 * k_blocks : sa_base0;
     sb_base =
         S::T128 ? reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * (g.rows_per_expert >> 7) * k_tiles * 4
                 : reinterpret_cast<const uint8_t*>(g.bs) + (size_t)e * g.rows_per_expert * k_blocks;
 #pragma unroll
     for (int q = 0; q < S::SA_INSTR; ++q) {
+      int srow;
       if constexpr (S::AS_COOP) {
-        sa_src[q] = (uint32_t)((32 * w + (ln & 31)) * k_blocks);
+        srow = 32 * w + (ln & 31);
         sa_dst[q] = (q * 256 + w * 64) * 4;                // term q, slot w
       } else {
         const int tm = q / (S::SA / 64), u = q % (S::SA / 64);
         const int rw = S::WROWS >= 64 ? 64 * u + ln : ln % S::WROWS;
-        sa_src[q] = (uint32_t)((wm * S::WROWS + rw) * k_blocks);
+        srow = wm * S::WROWS + rw;
         sa_dst[q] = ((w * TERMS + tm) * S::SA + 64 * u) * 4;
       }
+      const uint32_t src_row = GATEUP ? (uint32_t)token_of(row0 + srow) : (uint32_t)srow;
+      sa_src[q] = src_row * (uint32_t)k_blocks;
     }
 #pragma unroll
     for (int u = 0; u < S::SB_INSTR; ++u) {
@@ -747,12 +759,18 @@ hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const uint8_t* xs,
+                                  int T, int slots, const int32_t* sorted,
                                   const int32_t* expert_ids, const int32_t* npp, int capacity,
                                   int bs, uint8_t* hq, uint8_t* hs, hipStream_t s) {
-  if (capacity / bs == 0) return hipSuccess;
+  if (capacity / bs == 0 || T == 0) return hipSuccess;
+  // token row offsets are 32-bit in the kernel
+  if ((long long)T * W.hidden >= (1ll << 32)) return hipErrorNotSupported;
   GemmArgs a{};
   a.a = xq;
   a.as = xs;
+  a.sorted = sorted;
+  a.slots = slots;
+  a.sentinel = T * slots;
   a.b = reinterpret_cast<const uint8_t*>(W.w13);
   a.bs = W.w13_scale;
   a.expert_ids = expert_ids;

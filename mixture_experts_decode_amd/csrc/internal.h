@@ -38,10 +38,10 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int
                              int32_t* npp, void* ws, hipStream_t s);
 
 // grouped.hip
-hipError_t launch_gather_quant(const void* x, int x_dtype, int T, int H, int slots,
-                               const int32_t* sorted, const int32_t* npp, int capacity,
-                               uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_quant_rows(const void* x, int x_dtype, int T, int H, uint8_t* xq, uint8_t* xs,
+                             hipStream_t s);
 hipError_t launch_grouped_gate_up(const moe_weights& W, const uint8_t* xq, const uint8_t* xs,
+                                  int T, int slots, const int32_t* sorted,
                                   const int32_t* expert_ids, const int32_t* npp, int capacity,
                                   int bs, uint8_t* hq, uint8_t* hs, hipStream_t s);
 hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const uint8_t* hs,

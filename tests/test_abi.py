@@ -32,7 +32,7 @@ def lib():
 def test_headers_declare_the_boundary():
     names = declared_functions()
     for need in ("moe_align_sort", "moe_gate_up", "moe_down", "moe_layer", "moe_status_string",
-                 "moe_gather_quant", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
+                 "moe_quant_rows", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
                  "moe_choose_path", "moe_layer_workspace_bytes", "moe_util_copy"):
         assert need in names
 
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_sizes(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     # capacity = T*(k+S) + (E+S)*(BS-1)
     assert lib.moe_align_sort_capacity(16384, 8, 256, 0, 128) == 131072 + 256 * 127
     assert lib.moe_align_sort_capacity(3, 2, 4, 0, 4) == 6 + 4 * 3
@@ -117,8 +117,12 @@ def test_host_argument_errors(lib):
     assert lib.moe_topk_route(dummy, None, 4, 128, 8, dummy, None, None) == moe.ERR_INVALID_ARG
     assert lib.moe_topk_route(None, None, 0, 128, 8, None, None, None) == moe.OK
     # grouped steps reject fp32 weights
-    assert lib.moe_grouped_gate_up(ctypes.byref(_weights(moe, format=0)), dummy, dummy, dummy, dummy,
-                                   64, 64, dummy, dummy, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_grouped_gate_up(ctypes.byref(_weights(moe, format=0)), dummy, dummy, 4, 8, dummy,
+                                   dummy, dummy, 64, 64, dummy, dummy, None) == moe.ERR_UNSUPPORTED
+    # quant_rows: H must be a multiple of 32; T == 0 is a no-op
+    assert lib.moe_quant_rows(dummy, 1, 4, 100, dummy, dummy, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_quant_rows(None, 1, 0, 128, None, None, None) == moe.OK
+    assert lib.moe_quant_rows(dummy, 1, 4, 128, None, dummy, None) == moe.ERR_INVALID_ARG
 
 
 def test_path_choice_host_logic(lib):

@@ -26,9 +26,10 @@ def _bf16_tensor(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def test_gather_quant_all_bf16_values_bit_exact(lib):
+def test_quant_rows_all_bf16_values_bit_exact(lib):
     """Every finite BF16 value, in blocks whose maxima vary, quantises exactly
-    as the oracle's MX quantiser does (codes and scale bytes)."""
+    as the oracle's MX quantiser does (codes and scale bytes); each token row
+    is quantised once, in place of a gathered copy per slot."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = F.decode_bf16(bits)
     bits = bits[np.isfinite(vals)]
@@ -41,23 +42,24 @@ def test_gather_quant_all_bf16_values_bit_exact(lib):
     x = x.reshape(rows, h)
     x[-1, -64:] = 0                          # an all-zero block
     x[-1, -96] = 0x0001                      # a block holding only a subnormal
-    ids = np.arange(rows, dtype=np.int32)[:, None] % 3
-    sort = lib.align_sort(torch.from_numpy(ids).cuda(), 3, 0, 32)
-    xq, xs = lib.gather_quant(_bf16_tensor(x), 1, sort["sorted_token_ids"],
-                              sort["num_tokens_post_padded"], sort["capacity"])
+    xq, xs = lib.quant_rows(_bf16_tensor(x))
     torch.cuda.synchronize()
-    ref = A.align_sort(ids.reshape(-1), 3, 32)
-    npp = ref["num_tokens_post_padded"]
     codes, scales = F.quantize_mx_e4m3(F.decode_bf16(x))
-    for r in range(npp):
-        ent = ref["sorted_token_ids"][r]
-        got_q = xq[r].cpu().numpy()
-        got_s = xs[r].cpu().numpy()
-        if ent == rows:                       # padding row: zeros
-            assert not got_q.any() and not got_s.any()
-        else:
-            assert np.array_equal(got_q, codes[ent]), r
-            assert np.array_equal(got_s, scales[ent]), r
+    assert np.array_equal(xq.cpu().numpy(), codes)
+    assert np.array_equal(xs.cpu().numpy(), scales)
+
+
+def test_quant_rows_f32_input(lib):
+    """FP32 rows: the same rule on float32 values (a float32 value divided by
+    a power of two stays exact, so the oracle's float64 rule applies)."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((37, 512)) * np.exp(rng.uniform(-20, 20, (37, 1)))).astype(np.float32)
+    x[5, :32] = 0.0
+    xq, xs = lib.quant_rows(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    codes, scales = F.quantize_mx_e4m3(x.astype(np.float64))
+    assert np.array_equal(xq.cpu().numpy(), codes)
+    assert np.array_equal(xs.cpu().numpy(), scales)
 
 
 def _blocks_for(lib, ids, n_exp, bs):
@@ -70,32 +72,41 @@ def _blocks_for(lib, ids, n_exp, bs):
                                     ("mxfp4", 32), ("fp8_blk128", 128),
                                     ("mxfp4", 64), ("fp8_blk128", 32), ("fp8_blk128", 64)])
 def test_grouped_gate_up_alone(lib, fmt, bs):
-    """a7 on generator-made MXFP8 rows: h = SiLU(Wg a) * (Wu a) per block's
-    expert, requantised as hi = Q(h), lo = Q(h - hi).  The matrix core
-    accumulates with ~5e-5 relative error, so single codes may differ from
-    the float64 oracle's; hi + lo tracks h to ~2^-9 whatever hi chose."""
+    """a7 on generator-made MXFP8 token rows, two slots per token: every sorted
+    row reads its token's row (entry / slots), and h = SiLU(Wg a) * (Wu a) per
+    block's expert is requantised as hi = Q(h), lo = Q(h - hi).  The matrix
+    core accumulates with ~5e-5 relative error, so single codes may differ
+    from the float64 oracle's; hi + lo tracks h to ~2^-9 whatever hi chose."""
     cfg = SMALL[fmt].replace(num_shared=0)
     rng = np.random.default_rng(3)
-    ids = rng.integers(0, cfg.num_experts, size=(150, 1)).astype(np.int32)
+    t, slots = 75, 2
+    ids = np.stack([rng.permutation(cfg.num_experts)[:slots] for _ in range(t)]).astype(np.int32)
     sort = _blocks_for(lib, ids, cfg.num_experts, bs)
     cap = sort["capacity"]
-    xq_np, xs_np = W.mxfp8_rows(cfg, cap, cfg.hidden)
+    xq_np, xs_np = W.mxfp8_rows(cfg, t, cfg.hidden)
     Wd = device_weights(cfg)
     hq, hs = lib.grouped_gate_up(Wd, torch.from_numpy(xq_np).cuda(), torch.from_numpy(xs_np).cuda(),
-                                 sort["expert_ids"], sort["num_tokens_post_padded"], cap, bs)
+                                 t, slots, sort["sorted_token_ids"], sort["expert_ids"],
+                                 sort["num_tokens_post_padded"], cap, bs)
     torch.cuda.synchronize()
     ref = A.align_sort(ids.reshape(-1), cfg.num_experts, bs)
     npp = ref["num_tokens_post_padded"]
+    srt = np.asarray(ref["sorted_token_ids"][:npp])
+    real = srt < t * slots                   # padding rows carry no token
     get = expert_getter(cfg)
-    a = F.dequant_mx(xq_np[:npp], xs_np[:npp], "e4m3")
+    a_tok = F.dequant_mx(xq_np, xs_np, "e4m3")
     hq_np, hs_np = hq.cpu().numpy(), hs.cpu().numpy()
-    hi = F.dequant_mx(hq_np[0, :npp], hs_np[0, :npp], "e4m3")
-    got = hi + F.dequant_mx(hq_np[1, :npp], hs_np[1, :npp], "e4m3")
-    want = np.zeros_like(got)
+    hi = F.dequant_mx(hq_np[0, :npp], hs_np[0, :npp], "e4m3")[real]
+    got = hi + F.dequant_mx(hq_np[1, :npp], hs_np[1, :npp], "e4m3")[real]
+    want = np.zeros((npp, cfg.inter))
     for b, e in enumerate(ref["expert_ids"]):
         wg, wu, _ = L.dequant_expert(cfg.fmt, get(int(e)))
-        rows = slice(b * bs, (b + 1) * bs)
-        want[rows] = L.silu(a[rows] @ wg.T) * (a[rows] @ wu.T)
+        rows = np.arange(b * bs, (b + 1) * bs)
+        rows = rows[real[rows]]
+        a = a_tok[srt[rows] // slots]
+        want[rows] = L.silu(a @ wg.T) * (a @ wu.T)
+    want = want[real]
+    hq_hi = hq_np[0, :npp][real]
     # against the oracle's own two-term form of its float64 h: each side is
     # within half a lo step of its own h (<= 2^-9 of the element, 2^-6 of the
     # block maximum), and where accumulation noise flips a hi code the two lo
@@ -110,7 +121,7 @@ def test_grouped_gate_up_alone(lib, fmt, bs):
     # hi codes agree with the oracle's Q(h) except where h sits within the
     # accumulation error of a rounding boundary
     ch, _ = F.quantize_mx_e4m3(want)
-    assert np.mean(hq_np[0, :npp] == ch) > 0.99
+    assert np.mean(hq_hi == ch) > 0.99
 
 
 @pytest.mark.parametrize("fmt,bs", [("mxfp8", 64), ("mxfp4", 128), ("fp8_blk128", 64), ("mxfp8", 128),
