@@ -245,7 +245,6 @@ def main():
         y = torch.empty((b, cfg.hidden), dtype=torch.float32, device=dev)
         h = torch.empty((b, slots, cfg.inter),
                         dtype=torch.float32 if h_dtype == "f32" else torch.bfloat16, device=dev)
-        variant = "expert" if b >= 4 else "token"
         dws = torch.empty(max(16, slots * b * cfg.hidden * 4), dtype=torch.uint8, device=dev)
 
         def step(i, ev=None):
@@ -257,7 +256,7 @@ def main():
                 moe.gate_up(L, d["x"], d["ids"], h=h)
                 if ev is not None:
                     ev[1].record(stream)
-                moe.down(L, h, d["ids"], d["wts"], y=y, variant=variant, workspace=dws)
+                moe.down(L, h, d["ids"], d["wts"], y=y, workspace=dws)
                 if ev is not None:
                     ev[2].record(stream)
             else:
@@ -333,11 +332,26 @@ def main():
             res["down_us"] = float(np.mean(dn)) * 1e3
             res["gate_up_GBps"] = gub / (sum(gu) * 1e-3) / 1e9
             res["gate_up_bytes_per_launch"] = gub / steps
+            # the down product alone in each of its launch shapes (identical
+            # bits): token-major buffers nothing; expert-major writes FP32 slot
+            # outputs and adds them in a combine kernel
+            res["down_variants_us"] = {}
+            for var in ("token", "expert"):
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+                for i in range(steps):
+                    L, d = layers[i % n_layers], ins[i % n_layers]
+                    ev[i][0].record(stream)
+                    moe.down(L, h, d["ids"], d["wts"], y=y, variant=var, workspace=dws)
+                    ev[i][1].record(stream)
+                torch.cuda.synchronize()
+                res["down_variants_us"][var] = round(
+                    float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3, 2)
         log(f"{cfg.name} B={b} {chosen}: {res['us_per_layer']:.1f} us, {res['TBps']:.3f} TB/s, "
             f"parity {par}")
         return res
 
-    main_res = run_steps(B, args.steps, args.warmup, args.path, n_check=None)
+    # every token is checked up to B = 64; a spread of tokens beyond
+    main_res = run_steps(B, args.steps, args.warmup, args.path, n_check=None if B <= 64 else 4)
 
     sweep = []
     if not args.no_sweep and not args.headline_only and cfg is W.QWEN3_DECODE_MXFP8:
@@ -345,7 +359,7 @@ def main():
             r = run_steps(b, 50, 5, args.path, n_check=None)
             sweep.append(rounded(r, ("B", "path", "us_per_layer", "eager_us_per_layer", "replays_us",
                                      "TBps", "frac_of_copy_peak", "U_mean", "gate_up_us",
-                                     "down_us", "parity")))
+                                     "down_us", "down_variants_us", "parity")))
 
     roofline = None
     if main_res["path"] == "decode":
@@ -439,6 +453,7 @@ def main():
         "frac_of_copy_peak": None if copy_peak is None else round(value / copy_peak, 4),
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(main_res[k], 2) for k in ("gate_up_us", "down_us") if k in main_res},
+        "down_variants_us": main_res.get("down_variants_us"),
         "sweep": sweep,
         "layers": layers_sweep,
         "roofline": roofline,

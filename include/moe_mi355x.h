@@ -130,6 +130,14 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
                        const int32_t* topk_ids, int32_t T, int32_t k,
                        void* h, int32_t h_dtype, void* stream);
 
+/* Launch shapes of moe_down (all give identical bits). */
+typedef enum {
+  MOE_DOWN_AUTO = 0,          /* token-major up to 16 tokens, else expert-major   */
+  MOE_DOWN_TOKEN_MAJOR = 1,   /* a wavefront owns (token, rows); no buffer        */
+  MOE_DOWN_EXPERT_MAJOR = 2   /* a wavefront owns (expert, rows); slot buffer in
+                                 the workspace and a combine kernel               */
+} moe_down_variant;
+
 /*
  * moe_down: y[t][d] = sum_j w_tj * (Wd[e_tj][d,:] . h[t][j][:]) for every
  * token t < T and output d < H (warp-decode post, section on how the two
@@ -137,26 +145,33 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
  * the token's experts, folds each routing weight in and finishes with a
  * butterfly reduction; the combine is part of the projection).
  * Each slot's dot product is computed by a fixed group of lanes in a fixed
- * order, multiplied by w_tj, and the slots are added in slot order.  Two
- * launch shapes give identical bits:
- *   workspace == NULL  token-major: a wavefront owns (token, output rows) and
- *                      sums the slots in registers; nothing is buffered;
- *   workspace != NULL  expert-major: a wavefront owns (expert, output rows),
- *                      reads those rows once for all tokens routed to the
- *                      expert and stores w * dot per (token, slot) in the
- *                      workspace; a combine kernel adds them in slot order.
+ * order, multiplied by w_tj, and the slots are added in slot order, so every
+ * launch shape gives identical bits:
+ *   MOE_DOWN_TOKEN_MAJOR   a wavefront owns (token, output rows) and sums the
+ *                          slots in registers (the page's form); nothing is
+ *                          buffered;
+ *   MOE_DOWN_EXPERT_MAJOR  a wavefront owns (expert, output rows), reads those
+ *                          rows once for all tokens routed to the expert and
+ *                          stores w * dot per (token, slot) in the workspace;
+ *                          a combine kernel adds them in slot order.
+ *   MOE_DOWN_AUTO          token-major up to 16 tokens, expert-major beyond
+ *                          (measured faster on each side of that line).
  *   h            device, [T][slots][I], h_dtype
  *   topk_ids     device, [T][k] int32; topk_weights device, [T][k] float32
  *   y            device, [T][H], y_dtype
- *   workspace    device or NULL; if not NULL at least
- *                moe_down_workspace_bytes(W, T, k) bytes, 16-byte aligned
- * slots must be <= 64.
+ *   variant      moe_down_variant
+ *   workspace    device, at least moe_down_workspace_bytes(W, T, k) bytes,
+ *                16-byte aligned, when the variant run is expert-major;
+ *                ignored (may be NULL) otherwise
+ * slots must be <= 64; the expert-major shape takes at most
+ * moe_decode_max_entries() entries (MOE_ERR_UNSUPPORTED otherwise, before
+ * any launch).
  */
 size_t moe_down_workspace_bytes(const moe_weights* W, int32_t T, int32_t k);
 
 moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
                     const int32_t* topk_ids, const float* topk_weights,
-                    int32_t T, int32_t k, void* y, int32_t y_dtype,
+                    int32_t T, int32_t k, void* y, int32_t y_dtype, int32_t variant,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ */

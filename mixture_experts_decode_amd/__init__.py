@@ -21,6 +21,7 @@ DT = {"f32": 0, "bf16": 1}
 FMT = {"f32": 0, "mxfp8": 1, "mxfp4": 2, "fp8_blk128": 3}
 PATH = {"auto": 0, "decode": 1, "grouped": 2}
 PATH_NAME = {v: k for k, v in PATH.items()}
+DOWN_VARIANT = {"auto": 0, "token": 1, "expert": 2}
 
 _lib = None
 
@@ -50,7 +51,7 @@ _SIGS = {
     "moe_decode_max_entries": (_I, []),
     "moe_gate_up": (_I, [_WP, _P, _I, _P, _I, _I, _P, _I, _P]),
     "moe_down_workspace_bytes": (_Z, [_WP, _I, _I]),
-    "moe_down": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _P, _Z, _P]),
+    "moe_down": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _Z, _P]),
     "moe_align_sort_capacity": (_Z, [_I, _I, _I, _I, _I]),
     "moe_align_sort_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "moe_align_sort": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
@@ -184,23 +185,21 @@ def gate_up(W, x, topk_ids, h=None, h_dtype="f32", stream=None):
 @_on_stream
 def down(W, h, topk_ids, topk_weights, y=None, y_dtype="f32", variant="auto", workspace=None,
          stream=None):
-    """y [T][H] for the decode path.  variant: "token" (no workspace),
-    "expert" (expert-major with a slot buffer) or "auto" (expert-major from a
-    few tokens up, as moe_layer does).  Both variants give identical bits."""
+    """y [T][H] for the decode path.  variant: "token" (token-major), "expert"
+    (expert-major with a slot buffer in `workspace`) or "auto" (as moe_layer
+    does).  Every variant gives identical bits."""
     load()
     t, k = topk_ids.shape
     if y is None:
         y = _alloc((t, W.hidden), y_dtype, h.device)
-    if variant == "auto":
-        variant = "expert" if t >= 4 else "token"
     ws, wsb = None, 0
-    if variant == "expert":
+    if variant == "expert" or (variant == "auto" and t > 16):
         wsb = _lib.moe_down_workspace_bytes(W.ref, t, k)
         if workspace is None:
             workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=h.device)
         ws, wsb = _ptr(workspace), workspace.numel() * workspace.element_size()
     st = _lib.moe_down(W.ref, _ptr(h), _dt(h), _ptr(topk_ids), _ptr(topk_weights), t, k, _ptr(y),
-                       _dt(y), ws, wsb, _stream(stream))
+                       _dt(y), DOWN_VARIANT[variant], ws, wsb, _stream(stream))
     _check(st, "moe_down")
     return y
 

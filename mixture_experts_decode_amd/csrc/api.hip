@@ -16,7 +16,7 @@ namespace {
 using moe::kDecodeMaxEntries;
 using moe::kMaxExpertsTotal;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -162,8 +162,15 @@ size_t decode_h_bytes(const moe_weights* W, int32_t T, int32_t k) {
   return align_up((size_t)T * (k + W->num_shared) * W->inter * el);
 }
 
+// The decode path's workspace: h, then (for the expert-major down variant,
+// used from 17 tokens up) the FP32 slot outputs.
+size_t decode_slot_bytes(const moe_weights* W, int32_t T, int32_t k) {
+  if (moe::down_auto_variant(*W, T, k) != MOE_DOWN_EXPERT_MAJOR) return 0;
+  return align_up((size_t)T * (k + W->num_shared) * W->hidden * 4);
+}
+
 size_t decode_workspace(const moe_weights* W, int32_t T, int32_t k) {
-  return decode_h_bytes(W, T, k) + align_up((size_t)T * (k + W->num_shared) * W->hidden * 4);
+  return decode_h_bytes(W, T, k) + decode_slot_bytes(W, T, k);
 }
 
 // ---- workspace held by the library, for callers that cannot allocate -----
@@ -242,25 +249,27 @@ size_t moe_down_workspace_bytes(const moe_weights* W, int32_t T, int32_t k) {
 
 moe_status moe_down(const moe_weights* W, const void* h, int32_t h_dtype,
                     const int32_t* topk_ids, const float* topk_weights, int32_t T, int32_t k,
-                    void* y, int32_t y_dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    void* y, int32_t y_dtype, int32_t variant, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   moe_status st = check_weights(W);
   if (st != MOE_OK) return st;
   if ((st = check_routing(W, T, k)) != MOE_OK) return st;
   if (!dtype_ok(h_dtype) || !dtype_ok(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (variant < MOE_DOWN_AUTO || variant > MOE_DOWN_EXPERT_MAJOR) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!h || !y || (k > 0 && (!topk_ids || !topk_weights)) || !aligned16(h))
     return MOE_ERR_INVALID_ARG;
   if (h_dtype == MOE_DT_BF16 && W->format == MOE_W_F32) return MOE_ERR_UNSUPPORTED;
   if (k + W->num_shared > 64) return MOE_ERR_UNSUPPORTED;   // one slot per lane
   if (moe::down_lanes_per_row(W->format, W->inter, h_dtype) == 0) return MOE_ERR_UNSUPPORTED;
-  if (workspace) {
+  if (variant == MOE_DOWN_AUTO) variant = moe::down_auto_variant(*W, T, k);
+  if (variant == MOE_DOWN_EXPERT_MAJOR) {
+    if (!workspace) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < moe_down_workspace_bytes(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
-    if ((int64_t)T * (k + W->num_shared) > kDecodeMaxEntries) return MOE_ERR_UNSUPPORTED;
   }
   return from_hip(moe::launch_down_decode(*W, h, h_dtype, topk_ids, topk_weights, T, k, y,
-                                          y_dtype, reinterpret_cast<float*>(workspace),
+                                          y_dtype, variant, reinterpret_cast<float*>(workspace),
                                           as_stream(stream)));
 }
 
@@ -377,7 +386,7 @@ int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
   if (!grouped_supported(W) || W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;
   // a path the decode kernels refuse (too many entries to stage on chip, more
   // than 64 slots, a row length with no compiled shape) is never picked
-  if (moe::decode_supported(*W, T, k, decode_h_dtype(W), moe::down_expert_major(T)) != hipSuccess)
+  if (moe::decode_supported(*W, T, k, decode_h_dtype(W)) != hipSuccess)
     return MOE_PATH_GROUPED;
   return model_path(W, T, k);
 }
@@ -415,16 +424,14 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
     if (!aligned16(workspace) || !aligned16(x)) return MOE_ERR_INVALID_ARG;
     if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
     const int32_t hdt = decode_h_dtype(W);
-    // expert-major down from a few tokens up (identical results either way)
-    const bool em = moe::down_expert_major(T);
     // every shape limit of both kernels is checked before the first launch
-    if (moe::decode_supported(*W, T, k, hdt, em) != hipSuccess) return MOE_ERR_UNSUPPORTED;
+    if (moe::decode_supported(*W, T, k, hdt) != hipSuccess) return MOE_ERR_UNSUPPORTED;
     st = moe_gate_up(W, x, x_dtype, topk_ids, T, k, workspace, hdt, stream);
     if (st != MOE_OK) return st;
-    char* so = reinterpret_cast<char*>(workspace) + decode_h_bytes(W, T, k);
-    return moe_down(W, workspace, hdt, topk_ids, topk_weights, T, k, y, y_dtype,
-                    em ? so : nullptr, em ? workspace_bytes - decode_h_bytes(W, T, k) : 0,
-                    stream);
+    const size_t hb = decode_h_bytes(W, T, k);
+    const size_t sb = decode_slot_bytes(W, T, k);
+    return moe_down(W, workspace, hdt, topk_ids, topk_weights, T, k, y, y_dtype, MOE_DOWN_AUTO,
+                    sb ? reinterpret_cast<char*>(workspace) + hb : nullptr, sb, stream);
   }
   // grouped
   if (block_size == 0) block_size = auto_block(W, T, k);

@@ -24,8 +24,8 @@
 //      - expert-major: a wavefront owns (expert, output rows), reads those
 //        rows once and writes w * dot for every (token, slot) routed to the
 //        expert; a small combine kernel then sums the slots in slot order.
-//        Used from a few tokens up, because rows shared by several tokens do
-//        not survive in the 4 MB per-XCD L2 between the tokens' reads.
+//        Used from 17 tokens up, where it was measured faster: rows shared by
+//        several tokens are read once instead of once per (token, slot).
 //  * 16-byte loads per lane; E4M3 / E2M1 are converted exactly to BF16 and
 //    multiplied with BF16 activations by v_dot2_f32_bf16, or converted to FP32
 //    for FP32 intermediates; the MX / tile scale multiplies each 16-byte
@@ -44,6 +44,8 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaskWords = kMaxExpertsTotal / 32;
+constexpr int kDownTokenMajor = MOE_DOWN_TOKEN_MAJOR;
+constexpr int kDownExpertMajor = MOE_DOWN_EXPERT_MAJOR;
 
 // Occupancy floor for the streaming kernels: at least WPE wavefronts per SIMD
 // (4 -> <= 128 VGPRs), so latency is hidden by resident waves rather than by
@@ -102,9 +104,10 @@ __device__ __forceinline__ int stage_routing(const int32_t* ids, int k, int slot
                                              int n_words, int n_entries, int* s_ids,
                                              uint32_t* s_mask) {
   const int tid = threadIdx.x;
-  for (int q = tid; q < n_words; q += kBlock) s_mask[q] = 0;
+  const int nt = blockDim.x;
+  for (int q = tid; q < n_words; q += nt) s_mask[q] = 0;
   __syncthreads();
-  for (int v = tid; v < n_entries; v += kBlock) {
+  for (int v = tid; v < n_entries; v += nt) {
     const int t = v / slots, j = v - t * slots;
     const int e = j < k ? clamp_expert(ids[t * k + j], E) : E;
     s_ids[v] = e;
@@ -426,14 +429,19 @@ __device__ __forceinline__ void load_down_row(DownRow<FMT, CPL>& R, const DownAr
 // dot(row r, h[pe]) for the lane's RPL rows, each reduced over its LPR lanes
 // (every lane of the group gets the totals).  Fixed order per row: chunk by
 // chunk per lane, then the DPP tree; the staged h chunks serve all RPL rows.
-template <int FMT, int LPR, int CPL, int RPL, bool HBF16>
-__device__ __forceinline__ void down_rows_dot(DownRow<FMT, CPL> (&R)[RPL], const DownArgs& a,
-                                              int pe, int gl, float (&out)[RPL]) {
+template <int FMT, int LPR, int CPL, bool HBF16>
+__device__ __forceinline__ void load_h_chunks(XChunk<FMT, !HBF16> (&hc)[CPL], const DownArgs& a,
+                                              int pe, int gl) {
   const size_t h_row_bytes = (size_t)a.I * (HBF16 ? 2 : 4);
   const char* hrow = reinterpret_cast<const char*>(a.h) + (size_t)pe * h_row_bytes;
-  XChunk<FMT, !HBF16> hc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) load_x_chunk<FMT, !HBF16>(hc[i], hrow, gl + LPR * i);
+}
+
+template <int FMT, int LPR, int CPL, int RPL, bool HBF16>
+__device__ __forceinline__ void rows_dot_staged(DownRow<FMT, CPL> (&R)[RPL],
+                                                const XChunk<FMT, !HBF16> (&hc)[CPL],
+                                                float (&out)[RPL]) {
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
 #pragma unroll
@@ -447,6 +455,14 @@ __device__ __forceinline__ void down_rows_dot(DownRow<FMT, CPL> (&R)[RPL], const
     else if constexpr (LPR == 8) out[r] = group8_sum(acc);
     else out[r] = group4_sum(acc);
   }
+}
+
+template <int FMT, int LPR, int CPL, int RPL, bool HBF16>
+__device__ __forceinline__ void down_rows_dot(DownRow<FMT, CPL> (&R)[RPL], const DownArgs& a,
+                                              int pe, int gl, float (&out)[RPL]) {
+  XChunk<FMT, !HBF16> hc[CPL];
+  load_h_chunks<FMT, LPR, CPL, HBF16>(hc, a, pe, gl);
+  rows_dot_staged<FMT, LPR, CPL, RPL, HBF16>(R, hc, out);
 }
 
 __device__ __forceinline__ float slot_weight(const DownArgs& a, int pe) {
@@ -606,8 +622,9 @@ hipError_t gate_up_nr(const GateUpArgs& a, int nr, bool pre, int mch, bool guard
 }
 
 template <int FMT, int LPR, int CPL, bool HBF16>
-hipError_t down_launch(const DownArgs& a, bool expert_major, int ybf16, int blocks, hipStream_t s) {
+hipError_t down_launch(const DownArgs& a, int variant, int ybf16, int blocks, hipStream_t s) {
   dim3 g(blocks), b(kBlock);
+  const bool expert_major = variant == kDownExpertMajor;
   // rows per lane group as the register rule allows (4 up to 3 chunks per
   // lane, 2 up to 4); nothing wider is compiled
   if constexpr (CPL <= 3) {
@@ -632,7 +649,7 @@ hipError_t down_launch(const DownArgs& a, bool expert_major, int ybf16, int bloc
 }
 
 template <int FMT, int LPR, bool HBF16>
-hipError_t down_cpl(const DownArgs& a, bool em, int ybf16, int blocks, hipStream_t s) {
+hipError_t down_cpl(const DownArgs& a, int em, int ybf16, int blocks, hipStream_t s) {
   switch (a.cpl) {
     case 2: return down_launch<FMT, LPR, 2, HBF16>(a, em, ybf16, blocks, s);
     case 3: return down_launch<FMT, LPR, 3, HBF16>(a, em, ybf16, blocks, s);
@@ -646,7 +663,7 @@ hipError_t down_cpl(const DownArgs& a, bool em, int ybf16, int blocks, hipStream
 }
 
 template <int FMT, bool HBF16>
-hipError_t down_shape(const DownArgs& a, int lpr, bool em, int ybf16, int blocks, hipStream_t s) {
+hipError_t down_shape(const DownArgs& a, int lpr, int em, int ybf16, int blocks, hipStream_t s) {
   if (lpr == 4) return down_cpl<FMT, 4, HBF16>(a, em, ybf16, blocks, s);
   if (lpr == 8) return down_cpl<FMT, 8, HBF16>(a, em, ybf16, blocks, s);
   if (lpr == 16) return down_cpl<FMT, 16, HBF16>(a, em, ybf16, blocks, s);
@@ -687,7 +704,7 @@ struct GateUpPlan {
 struct DownPlan {
   DownArgs a;
   int lpr, blocks;
-  bool em;
+  int variant;     // kDownTokenMajor, kDownRowBlock or kDownExpertMajor
 };
 
 hipError_t plan_gate_up(const moe_weights& W, const void* x, const int32_t* ids, int T, int k,
@@ -775,12 +792,11 @@ int down_lanes_per_row(int fmt, int inter, int h_dtype) {
   return lanes_per_row_for(fmt, inter, h_dtype);
 }
 
-bool down_expert_major(int T) { return T >= 4; }
-
 namespace {
 
 hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int32_t* ids,
-                     const float* wts, int T, int k, void* y, float* slot_out, DownPlan& p) {
+                     const float* wts, int T, int k, void* y, int variant, float* slot_out,
+                     DownPlan& p) {
   DownArgs& a = p.a;
   a.w2 = reinterpret_cast<const uint8_t*>(W.w2);
   a.w2s = W.w2_scale;
@@ -795,16 +811,18 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
   a.I = W.inter;
   a.row_bytes = row_bytes_of(W.format, W.inter);
   a.chunks = a.row_bytes / 16;
-  p.em = slot_out != nullptr;
   // one slot per lane in the token-major kernel
   if (a.slots > kWave) return hipErrorNotSupported;
+  if (variant == kDownExpertMajor && slot_out == nullptr) return hipErrorInvalidValue;
+  p.variant = variant;
+  const bool em = variant == kDownExpertMajor;
   p.lpr = lanes_per_row_for(W.format, W.inter, h_dtype);
   if (p.lpr == 0) return hipErrorNotSupported;
   // row offsets inside one expert are 32-bit in the kernels
   if ((long long)a.H * a.row_bytes >= (1ll << 32)) return hipErrorNotSupported;
   a.n_entries = T * a.slots;
   // the expert-major kernel stages the routed ids on chip
-  if (p.em && a.n_entries > kDecodeMaxEntries) return hipErrorNotSupported;
+  if (em && a.n_entries > kDecodeMaxEntries) return hipErrorNotSupported;
   a.cpl = a.chunks / p.lpr;
   const int nd = kWave / p.lpr;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
@@ -815,12 +833,12 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
   const int hregs = a.cpl * elems * (h_dtype == MOE_DT_BF16 ? 2 : 4) / 4;
   const int rpl_fit = 4 * a.cpl * 5 + hregs <= 96 ? 4 : 2 * a.cpl * 5 + hregs <= 80 ? 2 : 1;
   const int rpl_max = a.cpl <= 3 ? 4 : a.cpl <= 4 ? 2 : 1;
-  a.rpl = p.em ? std::min(rpl_fit, rpl_max) : 1;
+  a.rpl = em ? std::min(rpl_fit, rpl_max) : 1;
   a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
   a.nxcd = device_num_xcds();
-  if (p.em) {
+  if (em) {
     a.y = slot_out;
     const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_dgroups;
     const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -836,16 +854,28 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
 
 }  // namespace
 
+// Token-major up to 16 tokens, expert-major beyond (and within the entries
+// it stages).  Measured on the Qwen3-style layer (down alone, MI355X): B = 4,
+// 8, 16: 13.1 / 22.6 / 36.7 us token-major against 17.4 / 27.0 / 38.1
+// expert-major; B = 32: 59.4 against 53.8 (the expert-major rows are read
+// once for all the tokens routed to them; the token-major ones once per
+// (token, slot), from L2 after the first).
+int down_variant_for(const moe_weights& W, int T, int k) {
+  const long long entries = (long long)T * (k + W.num_shared);
+  return T > 16 && entries <= kDecodeMaxEntries ? kDownExpertMajor : kDownTokenMajor;
+}
+
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               const int32_t* ids, const float* wts, int T, int k, void* y,
-                              int y_dtype, float* slot_out, hipStream_t s) {
+                              int y_dtype, int variant, float* slot_out, hipStream_t s) {
+  if (variant == MOE_DOWN_AUTO) variant = down_variant_for(W, T, k);
   DownPlan p;
-  hipError_t err = plan_down(W, h, h_dtype, ids, wts, T, k, y, slot_out, p);
+  hipError_t err = plan_down(W, h, h_dtype, ids, wts, T, k, y, variant, slot_out, p);
   if (err != hipSuccess) return err;
   const DownArgs& a = p.a;
   const bool hbf = h_dtype == MOE_DT_BF16;
   const int ybf = y_dtype == MOE_DT_BF16;
-  const bool em = p.em;
+  const int em = p.variant;
   switch (W.format) {
     case W_F32:
       err = hbf ? down_shape<W_F32, true>(a, p.lpr, em, ybf, p.blocks, s)
@@ -866,18 +896,20 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
     default:
       return hipErrorInvalidValue;
   }
-  if (err != hipSuccess || !em) return err;
+  if (err != hipSuccess || p.variant != kDownExpertMajor) return err;
   return launch_combine(slot_out, MOE_DT_F32, T, a.slots, W.hidden, y, y_dtype, s);
 }
 
-hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype, bool expert_major) {
+hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype) {
   GateUpPlan g;
   hipError_t e = plan_gate_up(W, nullptr, nullptr, T, k, nullptr, g);
   if (e != hipSuccess) return e;
   DownPlan d;
-  static float dummy;
-  return plan_down(W, nullptr, h_dtype, nullptr, nullptr, T, k, nullptr,
-                   expert_major ? &dummy : nullptr, d);
+  static float slot_dummy;   // stands for a slot buffer; nothing is launched
+  return plan_down(W, nullptr, h_dtype, nullptr, nullptr, T, k, nullptr, down_variant_for(W, T, k),
+                   &slot_dummy, d);
 }
+
+int down_auto_variant(const moe_weights& W, int T, int k) { return down_variant_for(W, T, k); }
 
 }  // namespace moe

@@ -20,16 +20,17 @@ int device_num_xcds();
 hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtype,
                                  const int32_t* ids, int T, int k, void* h, int h_dtype,
                                  hipStream_t s);
-// slot_out (T*slots*H floats) selects the expert-major variant + combine;
-// nullptr runs the token-major variant.  Both give identical bits.
+// variant: a moe_down_variant; MOE_DOWN_AUTO picks one.  The expert-major
+// variant needs slot_out (T*slots*H floats); all variants give identical bits.
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                               const int32_t* ids, const float* wts, int T, int k, void* y,
-                              int y_dtype, float* slot_out, hipStream_t s);
+                              int y_dtype, int variant, float* slot_out, hipStream_t s);
 int down_lanes_per_row(int fmt, int inter, int h_dtype);
-bool down_expert_major(int T);
 // hipSuccess if both decode kernels accept this shape (the down kernel in the
-// expert-major variant or not), else hipErrorNotSupported; launches nothing
-hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype, bool expert_major);
+// variant MOE_DOWN_AUTO picks), else hipErrorNotSupported; launches nothing
+hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype);
+// the moe_down_variant MOE_DOWN_AUTO runs for T tokens
+int down_auto_variant(const moe_weights& W, int T, int k);
 
 // align_sort.hip
 size_t align_sort_workspace_bytes(int n_entries, int n_experts);

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_sizes(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     # capacity = T*(k+S) + (E+S)*(BS-1)
     assert lib.moe_align_sort_capacity(16384, 8, 256, 0, 128) == 131072 + 256 * 127
     assert lib.moe_align_sort_capacity(3, 2, 4, 0, 4) == 6 + 4 * 3
@@ -80,17 +80,24 @@ def test_host_argument_errors(lib):
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 0, dummy, 4, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
     # misaligned weight pointer, bad format, non-multiple-of-32 hidden
     assert lib.moe_down(ctypes.byref(_weights(moe, w13=17)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
-                        None, 0, None) == moe.ERR_INVALID_ARG
+                        0, None, 0, None) == moe.ERR_INVALID_ARG
     assert lib.moe_down(ctypes.byref(_weights(moe, format=9)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
-                        None, 0, None) == moe.ERR_INVALID_ARG
+                        0, None, 0, None) == moe.ERR_INVALID_ARG
     assert lib.moe_down(ctypes.byref(_weights(moe, hidden=2050)), dummy, 0, dummy, dummy, 4, 8, dummy,
-                        0, None, 0, None) == moe.ERR_UNSUPPORTED
+                        0, 0, None, 0, None) == moe.ERR_UNSUPPORTED
     # missing scales for a quantised format
     assert lib.moe_down(ctypes.byref(_weights(moe, w2_scale=None)), dummy, 0, dummy, dummy, 4, 8, dummy,
-                        0, None, 0, None) == moe.ERR_INVALID_ARG
-    # workspace given but too small
-    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, dummy, 64,
+                        0, 0, None, 0, None) == moe.ERR_INVALID_ARG
+    # bad variant; the expert-major variant's workspace missing or too small
+    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, 3, None, 0,
+                        None) == moe.ERR_INVALID_ARG
+    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, 2, None, 0,
+                        None) == moe.ERR_INVALID_ARG
+    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, 2, dummy, 64,
                         None) == moe.ERR_WORKSPACE_TOO_SMALL
+    # AUTO runs expert-major from 17 tokens up, which needs the workspace
+    assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 32, 8, dummy, 0, 0, None, 0,
+                        None) == moe.ERR_INVALID_ARG
     assert lib.moe_down_workspace_bytes(ctypes.byref(w), 4, 8) == 4 * 8 * 2048 * 4
     # T == 0 is a no-op
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 0, 8, dummy, 0, None) == moe.OK
@@ -153,8 +160,10 @@ def test_path_choice_host_logic(lib):
     # fp32 weights have no grouped path
     w32 = _weights(__import__("mixture_experts_decode_amd"), format=0)
     assert lib.moe_choose_path(ctypes.byref(w32), 16384, 8) == DEC
-    # workspace sizes: decode = h (T*slots*I, BF16) + slot outputs (T*slots*H*4)
+    # workspace sizes: decode = h (T*slots*I, BF16), plus the FP32 slot
+    # outputs of the expert-major down from 17 tokens up
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * (768 * 2 + 2048 * 4)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 16, 8, DEC, 64) == 16 * 8 * 768 * 2
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 64) > 0
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 48) == 0
     # block 0: the library picks by expected entries per expert (32 at 2 per
@@ -186,7 +195,7 @@ def test_layer_refuses_unsupported_decode_shapes_before_any_launch(lib):
     w = _weights(moe)
     assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 2, 65, dummy, 0, DEC, 0,
                          dummy, big, None, None) == moe.ERR_UNSUPPORTED
-    assert lib.moe_down(ctypes.byref(w), dummy, 1, dummy, dummy, 2, 65, dummy, 0, None, 0,
+    assert lib.moe_down(ctypes.byref(w), dummy, 1, dummy, dummy, 2, 65, dummy, 0, 0, None, 0,
                         None) == moe.ERR_UNSUPPORTED
     # AUTO never picks a path that cannot run
     assert lib.moe_choose_path(ctypes.byref(w), 2, 65) == GRP

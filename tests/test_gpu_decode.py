@@ -105,20 +105,39 @@ def test_batch_invariance_and_determinism(lib):
 
 
 @pytest.mark.parametrize("fmt", list(SMALL))
-def test_down_variants_bitwise_identical(lib, fmt):
+@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
+def test_down_variants_bitwise_identical(lib, fmt, h_dtype):
     """Token-major and expert-major down give the same bits (same per-slot
     lane groups and reduction tree, slots added in slot order)."""
     cfg = SMALL[fmt]
+    if fmt == "f32" and h_dtype == "bf16":
+        pytest.skip("FP32 weights take an FP32 h")
     t = 3 if fmt == "f32" else 13
     x, ids, w = inputs(cfg, t)
     Wd = device_weights(cfg)
     idd, wd = device_routing(ids, w)
-    h = lib.gate_up(Wd, to_device_x(cfg, x), idd)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd, h_dtype=h_dtype)
     for y_dtype in ("f32", "bf16"):
         y_tok = lib.down(Wd, h, idd, wd, y_dtype=y_dtype, variant="token")
-        y_exp = lib.down(Wd, h, idd, wd, y_dtype=y_dtype, variant="expert")
+        y_exp = torch.full_like(y_tok, float("nan"))
+        lib.down(Wd, h, idd, wd, y=y_exp, variant="expert")
         torch.cuda.synchronize()
-        assert torch.equal(y_tok, y_exp), (fmt, y_dtype)
+        assert torch.equal(y_tok, y_exp), (fmt, y_dtype, "expert")
+
+
+def test_expert_major_down_at_the_entry_limit(lib):
+    """The expert-major down on the most entries it stages (256 tokens x top-8
+    of the Qwen3-style layer) equals the token-major down bit for bit."""
+    cfg = W.QWEN3_DECODE_MXFP8
+    t = lib.load().moe_decode_max_entries() // cfg.top_k
+    x, ids, w = inputs(cfg, t)
+    Wd = device_weights(cfg)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd, h_dtype="bf16")
+    y_tok = lib.down(Wd, h, idd, wd, variant="token")
+    y_exp = lib.down(Wd, h, idd, wd, variant="expert")
+    torch.cuda.synchronize()
+    assert torch.equal(y_tok, y_exp)
 
 
 def test_every_output_written(lib):
