@@ -210,6 +210,21 @@ def test_grouped_layer_small(lib, fmt, t, bs):
     assert metrics(y, y_none)["rel_l2"] > metrics(y, y_ref)["rel_l2"]
 
 
+def test_grouped_block_size_does_not_change_the_bits(lib):
+    """Every output element is accumulated over K in the same order whatever
+    the tile, so the layer is bit for bit the same with 32, 64 and 128-row
+    blocks."""
+    cfg = SMALL["mxfp8"]
+    x, ids, w = inputs(cfg, 600)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    ys = [lib.layer(Wd, xd, idd, wd, path="grouped", block=bs)[0] for bs in (32, 64, 128)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0], y)
+
+
 def test_grouped_layer_deterministic(lib):
     cfg = SMALL["mxfp8"]
     _, _, _, y1 = _grouped_layer(lib, cfg, 100, 64)
