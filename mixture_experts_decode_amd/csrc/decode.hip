@@ -26,6 +26,10 @@
 //        expert; a small combine kernel then sums the slots in slot order.
 //        Used from 17 tokens up, where it was measured faster: rows shared by
 //        several tokens are read once instead of once per (token, slot).
+//  * MXFP4 gate_up (E2M1 rows, BF16 activations) runs on the matrix cores
+//    instead: a wavefront owns (expert, 16 neurons) with the expert's routed
+//    entries as MFMA columns, and streams 128-byte row slices through an LDS
+//    ring by direct-to-LDS loads (see gate_up_mx4_mfma_kernel).
 //  * 16-byte loads per lane; E4M3 / E2M1 are converted exactly to BF16 and
 //    multiplied with BF16 activations by v_dot2_f32_bf16, or converted to FP32
 //    for FP32 intermediates; the MX / tile scale multiplies each 16-byte
@@ -390,6 +394,276 @@ MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs 
       load_token_x<FMT, MCH, XF32, GUARD>(xc, a, pe, lane);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// gate_up on the matrix cores for E2M1 rows and BF16 activations
+// ---------------------------------------------------------------------------
+//
+// The vector kernel converts E2M1 rows again for every routed token (BF16
+// copies of its rows do not fit in registers), so its work grows with the
+// tokens per expert.  Here a wavefront owns (expert, 16 neurons): their 16
+// gate and 16 up rows are the MFMA row operand, and the expert's routed
+// (token, slot) entries are the column operand of v_mfma_f32_16x16x32_bf16,
+// kMx4Tc at a time (an expert with more entries takes several passes).
+// The rows are cut into 128-byte slices (256 K values).  A slice of the 32
+// rows, the activations of the pass's tokens over the same K range and the
+// rows' E8M0 scales travel HBM -> LDS by direct-to-LDS loads into a ring of
+// kMx4Ns stages per wavefront, so kMx4Ns - 1 stages are in flight while one
+// is consumed and no registers hold staged data.  Each slice is converted to
+// BF16 once (the MX scale, a power of two, enters the conversion exactly)
+// and serves every column.  A lane's A and B operands take the same K values
+// in the same order (a permutation of K that keeps each 16-byte chunk in one
+// lane), so each column is an exact-product FP32 accumulation over K in a
+// fixed order that does not depend on the other columns: h does not depend
+// on the batch.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMx4SliceBytes = 128;            // bytes of a row per stage (256 K values)
+constexpr int kMx4Tc = 8;                      // entries (MFMA columns) per pass
+constexpr int kMx4Ns = 4;                      // ring stages per wavefront
+constexpr int kMx4XBytes = 2 * 2 * kMx4SliceBytes;   // BF16 activations per token per stage
+// Stage: W [32 rows][128 B] (16-byte chunks XOR-swizzled by row) |
+//        X [kMx4Tc tokens][512 B] (16-byte pieces XOR-swizzled by token) |
+//        S [32 rows][2 dwords] (the eight E8M0 scales of the row's slice)
+constexpr int kMx4X = 32 * kMx4SliceBytes, kMx4S = kMx4X + kMx4Tc * kMx4XBytes;
+constexpr int kMx4Stage = kMx4S + 256;
+constexpr int kMx4XInstr = kMx4Tc * kMx4XBytes / 1024;
+constexpr int kMx4Ops = 4 + kMx4XInstr + 1;    // direct-to-LDS loads per stage
+static_assert((kMx4Ns - 2) * kMx4Ops < 64, "vmcnt range");
+constexpr int kMx4Lds = kWavesPerBlock * kMx4Ns * kMx4Stage + 4 * kDecodeMaxEntries +
+                        4 * kMaskWords + 4 * kWavesPerBlock * 2 * kMx4Tc;
+static_assert(kMx4Lds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ void dma16_lds(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_lds(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// Until at most N vector-memory operations of this wavefront are outstanding
+// (they complete in issue order) and all its LDS reads have returned.
+template <int N>
+__device__ __forceinline__ void wait_vmem_and_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
+// LDS slot of 16-byte chunk c of row r inside a 128-byte slice: a bijection
+// per row under which 16 consecutive rows reading one chunk hit distinct banks.
+__device__ __forceinline__ int mx4_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Entries of expert e with rank [kMx4Tc * pass, kMx4Tc * (pass + 1)) in entry
+// order -> list[0 .. kMx4Tc); returns the number of entries of e.  Whole
+// wavefront.
+__device__ __forceinline__ int mx4_pass_entries(const int* s_ids, int n_entries, int e, int pass,
+                                                int* list) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int seen = 0;
+  for (int b = 0; b < n_entries; b += kWave) {
+    const int v = b + lane;
+    const bool m = v < n_entries && s_ids[v] == e;
+    const unsigned long long bm = __ballot(m);
+    if (m) {
+      const int r = seen + __popcll(bm & ((1ull << lane) - 1ull)) - kMx4Tc * pass;
+      if (r >= 0 && r < kMx4Tc) list[r] = v;
+    }
+    seen += __popcll(bm);
+  }
+  return seen;
+}
+
+// Shapes the matrix-core kernel takes: whole 16-neuron blocks and whole
+// 128-byte row slices (I % 16 == 0, H % 256 == 0).
+bool gate_up_mx4_mfma_fits(const moe_weights& W) {
+  return W.inter % 16 == 0 && W.hidden % 256 == 0;
+}
+
+template <bool HBF16>
+__global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpArgs a) {
+  constexpr int kRing = kWavesPerBlock * kMx4Ns * kMx4Stage;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMx4Lds];
+  // one LDS array: the compiler then orders LDS reads against the
+  // direct-to-LDS loads only through the explicit waits below
+  int* s_ids = reinterpret_cast<int*>(lds + kRing);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + kRing + 4 * kDecodeMaxEntries);
+  int* s_lists = reinterpret_cast<int*>(lds + kRing + 4 * kDecodeMaxEntries + 4 * kMaskWords);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = wave_in_block();
+  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
+  const int n_nb = a.I >> 4;
+  const int n_units = U * n_nb;
+  const int n_waves = gridDim.x * kWavesPerBlock;
+  const int u_first = blockIdx.x * kWavesPerBlock + wv;
+  if (u_first >= n_units) return;
+  const int S = a.row_bytes / kMx4SliceBytes;   // stages per pass
+  const int n = lane & 15, g = lane >> 4;       // MFMA column / K group of this lane
+  const int scale_row = a.H >> 5;               // E8M0 bytes per row
+  int* list_i = s_lists + wv * 2 * kMx4Tc;      // entries of the pass being loaded
+  int* list_c = list_i + kMx4Tc;                // entries of the pass being computed
+  uint8_t* const ring = lds + wv * kMx4Ns * kMx4Stage;
+  const uint8_t* x8 = reinterpret_cast<const uint8_t*>(a.x);
+  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(a.w13s);
+
+  // Per-lane source offsets, fixed for the whole kernel.  Weights: load j
+  // fills stage rows 8j .. 8j+7 (rows 0-15 gate, 16-31 up), lane -> row
+  // 8j + lane/8, LDS slot lane%8 holding chunk (lane%8) ^ swz(row).
+  uint32_t w_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    w_off[j] = (uint32_t)(r & 15) * a.row_bytes + 16u * (uint32_t)((lane & 7) ^ mx4_swz(r));
+  }
+  // scales: lane -> row lane/2, dword lane%2 of the row's 8 scale bytes
+  const int s_row = lane >> 1, s_dw = lane & 1;
+
+  // ---- load cursor: unit (expert rank, neuron block), pass, stage ----
+  int iu = u_first, ipass = 0, is = 0, icnt = 0, ie = 0;
+  bool idone = false;
+  const uint8_t* iw_gate = nullptr;
+  const uint8_t* iw_up = nullptr;
+  const uint8_t* i_scale = nullptr;
+  const uint8_t* ix[kMx4XInstr];
+  // activations: load j, lane -> token slot t = (64j + lane) / 32, piece
+  // p = lane % 32 of its 512-byte slice, stored at piece slot p, holding
+  // piece p ^ (t % 16)
+  auto load_pass_tokens = [&]() {
+    const int have = icnt - kMx4Tc * ipass;
+#pragma unroll
+    for (int j = 0; j < kMx4XInstr; ++j) {
+      const int idx = 64 * j + lane;
+      const int t = idx >> 5, p = idx & 31;
+      const int pe = list_i[t < have ? t : 0];
+      ix[j] = x8 + (size_t)div_slots(pe, a.slots_magic) * a.H * 2 + 16 * (p ^ (t & 15));
+    }
+  };
+  auto load_unit = [&]() {
+    const int rank = iu / n_nb;
+    ie = select_rank(s_mask, a.n_words, rank);
+    const int nb = iu - rank * n_nb;
+    const long long r0 = (long long)ie * 2 * a.I + nb * 16;
+    iw_gate = a.w13 + r0 * a.row_bytes;
+    iw_up = a.w13 + (r0 + a.I) * a.row_bytes;
+    i_scale = s8 + (r0 + (s_row >> 4) * (long long)a.I + (s_row & 15)) * scale_row + 4 * s_dw;
+    icnt = mx4_pass_entries(s_ids, a.n_entries, ie, ipass, list_i);
+    load_pass_tokens();
+  };
+  load_unit();
+
+  // Every call issues kMx4Ops loads: after the last stage the cursor stays
+  // put and the loads repeat its addresses (in L2), so the waits are exact.
+  auto issue = [&](int q) {
+    const uint32_t so = (uint32_t)is * kMx4SliceBytes;
+    uint8_t* dst = ring + q * kMx4Stage;
+    dma16_lds(iw_gate + so + w_off[0], dst);
+    dma16_lds(iw_gate + so + w_off[1], dst + 1024);
+    dma16_lds(iw_up + so + w_off[2], dst + 2048);
+    dma16_lds(iw_up + so + w_off[3], dst + 3072);
+#pragma unroll
+    for (int j = 0; j < kMx4XInstr; ++j)
+      dma16_lds(ix[j] + (size_t)is * kMx4XBytes, dst + kMx4X + 1024 * j);
+    dma4_lds(i_scale + 8 * is, dst + kMx4S);
+    asm volatile("" ::: "memory");
+    if (!idone && ++is == S) {
+      is = 0;
+      if (kMx4Tc * (++ipass) < icnt) {
+        mx4_pass_entries(s_ids, a.n_entries, ie, ipass, list_i);
+        load_pass_tokens();
+      } else if (iu + n_waves < n_units) {
+        ipass = 0;
+        iu += n_waves;
+        load_unit();
+      } else {
+        idone = true;
+        is = S - 1;
+      }
+    }
+  };
+
+  // ---- compute cursor ----
+  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cnb = 0, ce = 0;
+  auto compute_unit = [&]() {
+    const int rank = cu / n_nb;
+    ce = select_rank(s_mask, a.n_words, rank);
+    cnb = cu - rank * n_nb;
+    ccnt = mx4_pass_entries(s_ids, a.n_entries, ce, cpass, list_c);
+  };
+  compute_unit();
+
+#pragma unroll
+  for (int q = 0; q < kMx4Ns - 1; ++q) issue(q);
+
+  f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
+  const int xt = n % kMx4Tc;   // token slot of this lane's column (columns >= kMx4Tc repeat)
+  bool cdone = false;
+  while (!cdone) {
+#pragma unroll
+    for (int q = 0; q < kMx4Ns; ++q) {
+      if (cdone) break;
+      wait_vmem_and_lds<(kMx4Ns - 2) * kMx4Ops>();
+      issue((q + kMx4Ns - 1) % kMx4Ns);
+      const uint8_t* st = ring + q * kMx4Stage;
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kMx4S);
+      const uint8_t* xrow = st + kMx4X + xt * kMx4XBytes;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {            // gate rows, then up rows
+        const int row = 16 * p + n;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int c = 4 * jj + g;            // 16-byte chunk: K 32c .. 32c+31 of the slice
+          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * kMx4SliceBytes +
+                                                          16 * (c ^ mx4_swz(row)));
+          const float scl = e8m0_to_f32((sc[2 * row + (c >> 2)] >> (8 * (c & 3))) & 0xffu);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {        // dword i: K 32c + 8i .. 32c + 8i + 7
+            const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 0);
+            const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 1);
+            const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 2);
+            const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 3);
+            const bf16x8 av = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            const int piece = 4 * c + i;
+            const bf16x8 xv = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(xrow + 16 * (piece ^ (xt & 15))));
+            if (p == 0) acc_g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc_g, 0, 0, 0);
+            else acc_u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc_u, 0, 0, 0);
+          }
+        }
+      }
+      if (++cs == S) {
+        // lane (n, g) holds neurons 4g .. 4g+3 of the block for column n
+        cs = 0;
+        const int have = ccnt - kMx4Tc * cpass;
+        if (n < have && n < kMx4Tc) {
+          const size_t off = (size_t)list_c[n] * a.I + cnb * 16 + 4 * g;
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = swiglu(acc_g[i], acc_u[i]);
+          if constexpr (HBF16) {
+            const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+            const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + off) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.h) + off) =
+                make_float4(o[0], o[1], o[2], o[3]);
+          }
+        }
+        acc_g = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_u = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kMx4Tc * (++cpass) < ccnt) {
+          mx4_pass_entries(s_ids, a.n_entries, ce, cpass, list_c);
+        } else if (cu + n_waves < n_units) {
+          cpass = 0;
+          cu += n_waves;
+          compute_unit();
+        } else {
+          cdone = true;
+        }
+      }
+    }
+  }
+  wait_vmem_and_lds<0>();   // no direct-to-LDS load may land after the wavefront ends
 }
 
 // ---------------------------------------------------------------------------
@@ -772,6 +1046,12 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
       return hbf ? gate_up_nr<W_MXFP8, false, true>(a, nr, pre, mch, guard, blocks, s)
                  : gate_up_nr<W_MXFP8, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_MXFP4:
+      if (!xf32 && gate_up_mx4_mfma_fits(W)) {
+        // one persistent workgroup per CU (the stage ring takes most of the LDS)
+        if (hbf) hipLaunchKernelGGL(gate_up_mx4_mfma_kernel<true>, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL(gate_up_mx4_mfma_kernel<false>, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
+        return hipGetLastError();
+      }
       return hbf ? gate_up_nr<W_MXFP4, false, true>(a, nr, pre, mch, guard, blocks, s)
                  : gate_up_nr<W_MXFP4, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_FP8B128:

@@ -82,10 +82,13 @@ def test_down_alone_on_given_h(lib):
     assert_layer_close(to_f64(y), ref)
 
 
-def test_batch_invariance_and_determinism(lib):
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_batch_invariance_and_determinism(lib, fmt):
     """Each output is produced by one wavefront in a fixed order, so a token's
-    h and y do not depend on the rest of the batch and repeat bit for bit."""
-    cfg = SMALL["mxfp8"]
+    h and y do not depend on the rest of the batch and repeat bit for bit
+    (MXFP4 gate_up runs on the matrix cores: a token's MFMA column does not
+    change its bits either)."""
+    cfg = SMALL[fmt]
     x, ids, w = inputs(cfg, 32)
     Wd = device_weights(cfg)
     xd = to_device_x(cfg, x)
@@ -241,3 +244,27 @@ def test_decode_at_the_entry_limit(lib):
     with pytest.raises(lib.MoeError) as err:
         lib.layer(Wd, to_device_x(cfg, x2), *device_routing(ids2, w2), path="decode")
     assert err.value.status == lib.ERR_UNSUPPORTED
+
+
+def test_mx4_matrix_core_passes_and_shared_expert(lib):
+    """MXFP4 gate_up on the matrix cores takes 8 entries of an expert per
+    pass: here every token's first slot goes to expert 3 (20 entries, three
+    passes), nine tokens also send slot 1 to expert 5, and a shared expert
+    adds one more slot per token."""
+    cfg = SMALL["mxfp4"].replace(num_shared=1, tag=24)
+    t = 20
+    x, ids, w = inputs(cfg, t)
+    ids = ids.copy()
+    ids[:, 0] = 3
+    ids[:9, 1] = 5
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, xd, idd)
+    y = lib.down(Wd, h, idd, wd)
+    torch.cuda.synchronize()
+    h_ref, y_ref = _oracle(cfg, x, ids, w)
+    scale = np.sqrt(np.mean(h_ref ** 2))
+    hh = to_f64(h)
+    assert np.max(np.abs(hh - h_ref)) <= 2e-4 * scale + 1e-6, np.max(np.abs(hh - h_ref)) / scale
+    assert_layer_close(to_f64(y), y_ref)
