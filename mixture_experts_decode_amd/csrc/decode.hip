@@ -455,11 +455,11 @@ __device__ __forceinline__ void wait_vmem_and_lds() {
 // per row under which 16 consecutive rows reading one chunk hit distinct banks.
 __device__ __forceinline__ int mx4_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Entries of expert e with rank [kMx4Tc * pass, kMx4Tc * (pass + 1)) in entry
-// order -> list[0 .. kMx4Tc); returns the number of entries of e.  Whole
-// wavefront.
-__device__ __forceinline__ int mx4_pass_entries(const int* s_ids, int n_entries, int e, int pass,
-                                                int* list) {
+// Entries of expert e with rank [TC * pass, TC * (pass + 1)) in entry order
+// -> list[0 .. TC); returns the number of entries of e.  Whole wavefront.
+template <int TC>
+__device__ __forceinline__ int pass_entries(const int* s_ids, int n_entries, int e, int pass,
+                                            int* list) {
   const int lane = threadIdx.x & (kWave - 1);
   int seen = 0;
   for (int b = 0; b < n_entries; b += kWave) {
@@ -467,8 +467,8 @@ __device__ __forceinline__ int mx4_pass_entries(const int* s_ids, int n_entries,
     const bool m = v < n_entries && s_ids[v] == e;
     const unsigned long long bm = __ballot(m);
     if (m) {
-      const int r = seen + __popcll(bm & ((1ull << lane) - 1ull)) - kMx4Tc * pass;
-      if (r >= 0 && r < kMx4Tc) list[r] = v;
+      const int r = seen + __popcll(bm & ((1ull << lane) - 1ull)) - TC * pass;
+      if (r >= 0 && r < TC) list[r] = v;
     }
     seen += __popcll(bm);
   }
@@ -495,9 +495,12 @@ __global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpAr
   const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
   const int n_nb = a.I >> 4;
   const int n_units = U * n_nb;
-  const int n_waves = gridDim.x * kWavesPerBlock;
-  const int u_first = blockIdx.x * kWavesPerBlock + wv;
-  if (u_first >= n_units) return;
+  // each wavefront takes a contiguous range of units, so consecutive units
+  // mostly share the expert (and its entry list) and read adjacent rows
+  const long long gw = (long long)blockIdx.x * kWavesPerBlock + wv;
+  const long long nw = (long long)gridDim.x * kWavesPerBlock;
+  const int u_first = (int)(gw * n_units / nw), u_end = (int)((gw + 1) * n_units / nw);
+  if (u_first >= u_end) return;
   const int S = a.row_bytes / kMx4SliceBytes;   // stages per pass
   const int n = lane & 15, g = lane >> 4;       // MFMA column / K group of this lane
   const int scale_row = a.H >> 5;               // E8M0 bytes per row
@@ -539,16 +542,22 @@ __global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpAr
       ix[j] = x8 + (size_t)div_slots(pe, a.slots_magic) * a.H * 2 + 16 * (p ^ (t & 15));
     }
   };
+  int irank = -1;
   auto load_unit = [&]() {
     const int rank = iu / n_nb;
-    ie = select_rank(s_mask, a.n_words, rank);
     const int nb = iu - rank * n_nb;
+    // a new expert, or one whose entries took several passes: find pass 0
+    const bool relist = rank != irank || icnt > kMx4Tc;
+    if (rank != irank) ie = select_rank(s_mask, a.n_words, rank);
+    irank = rank;
     const long long r0 = (long long)ie * 2 * a.I + nb * 16;
     iw_gate = a.w13 + r0 * a.row_bytes;
     iw_up = a.w13 + (r0 + a.I) * a.row_bytes;
     i_scale = s8 + (r0 + (s_row >> 4) * (long long)a.I + (s_row & 15)) * scale_row + 4 * s_dw;
-    icnt = mx4_pass_entries(s_ids, a.n_entries, ie, ipass, list_i);
-    load_pass_tokens();
+    if (relist) {
+      icnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
+      load_pass_tokens();
+    }
   };
   load_unit();
 
@@ -569,11 +578,11 @@ __global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpAr
     if (!idone && ++is == S) {
       is = 0;
       if (kMx4Tc * (++ipass) < icnt) {
-        mx4_pass_entries(s_ids, a.n_entries, ie, ipass, list_i);
+        pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
         load_pass_tokens();
-      } else if (iu + n_waves < n_units) {
+      } else if (iu + 1 < u_end) {
         ipass = 0;
-        iu += n_waves;
+        ++iu;
         load_unit();
       } else {
         idone = true;
@@ -583,12 +592,14 @@ __global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpAr
   };
 
   // ---- compute cursor ----
-  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cnb = 0, ce = 0;
+  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cnb = 0, ce = 0, crank = -1;
   auto compute_unit = [&]() {
     const int rank = cu / n_nb;
-    ce = select_rank(s_mask, a.n_words, rank);
     cnb = cu - rank * n_nb;
-    ccnt = mx4_pass_entries(s_ids, a.n_entries, ce, cpass, list_c);
+    const bool relist = rank != crank || ccnt > kMx4Tc;
+    if (rank != crank) ce = select_rank(s_mask, a.n_words, rank);
+    crank = rank;
+    if (relist) ccnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
   };
   compute_unit();
 
@@ -652,10 +663,10 @@ __global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpAr
         acc_g = f32x4{0.f, 0.f, 0.f, 0.f};
         acc_u = f32x4{0.f, 0.f, 0.f, 0.f};
         if (kMx4Tc * (++cpass) < ccnt) {
-          mx4_pass_entries(s_ids, a.n_entries, ce, cpass, list_c);
-        } else if (cu + n_waves < n_units) {
+          pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
+        } else if (cu + 1 < u_end) {
           cpass = 0;
-          cu += n_waves;
+          ++cu;
           compute_unit();
         } else {
           cdone = true;
