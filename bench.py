@@ -332,8 +332,8 @@ def main():
             res["down_us"] = float(np.mean(dn)) * 1e3
             res["gate_up_GBps"] = gub / (sum(gu) * 1e-3) / 1e9
             res["gate_up_bytes_per_launch"] = gub / steps
-            # the down product alone in each of its launch shapes (identical
-            # bits): token-major buffers nothing; expert-major writes FP32 slot
+            # the down product alone in each of its launch shapes:
+            # token-major buffers nothing; expert-major writes FP32 slot
             # outputs and adds them in a combine kernel
             res["down_variants_us"] = {}
             for var in ("token", "expert"):

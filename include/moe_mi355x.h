@@ -130,9 +130,11 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
                        const int32_t* topk_ids, int32_t T, int32_t k,
                        void* h, int32_t h_dtype, void* stream);
 
-/* Launch shapes of moe_down (all give identical bits). */
+/* Launch shapes of moe_down (identical bits, with the MXFP4 exception below). */
 typedef enum {
-  MOE_DOWN_AUTO = 0,          /* token-major up to 16 tokens, else expert-major   */
+  MOE_DOWN_AUTO = 0,          /* token-major up to 16 tokens, else expert-major;
+                                 expert-major at every T for MXFP4 rows that fit
+                                 the matrix-core kernel (see below)             */
   MOE_DOWN_TOKEN_MAJOR = 1,   /* a wavefront owns (token, rows); no buffer        */
   MOE_DOWN_EXPERT_MAJOR = 2   /* a wavefront owns (expert, rows); slot buffer in
                                  the workspace and a combine kernel               */
@@ -156,6 +158,12 @@ typedef enum {
  *                          a combine kernel adds them in slot order.
  *   MOE_DOWN_AUTO          token-major up to 16 tokens, expert-major beyond
  *                          (measured faster on each side of that line).
+ * The exception: MXFP4 weights with BF16 h, I a multiple of 256 and H of 32.
+ * Their expert-major shape runs on the matrix cores (the expert's routed
+ * entries as the columns of v_mfma_f32_16x16x32_bf16): the same exact
+ * products summed in another FP32 order, so its bits differ from the
+ * token-major shape's.  AUTO takes it at every T for such weights, so y still
+ * does not depend on the batch.
  *   h            device, [T][slots][I], h_dtype
  *   topk_ids     device, [T][k] int32; topk_weights device, [T][k] float32
  *   y            device, [T][H], y_dtype

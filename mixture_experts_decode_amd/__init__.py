@@ -187,13 +187,13 @@ def down(W, h, topk_ids, topk_weights, y=None, y_dtype="f32", variant="auto", wo
          stream=None):
     """y [T][H] for the decode path.  variant: "token" (token-major), "expert"
     (expert-major with a slot buffer in `workspace`) or "auto" (as moe_layer
-    does).  Every variant gives identical bits."""
+    does; it may pick either, so a slot buffer is passed)."""
     load()
     t, k = topk_ids.shape
     if y is None:
         y = _alloc((t, W.hidden), y_dtype, h.device)
     ws, wsb = None, 0
-    if variant == "expert" or (variant == "auto" and t > 16):
+    if variant in ("expert", "auto"):
         wsb = _lib.moe_down_workspace_bytes(W.ref, t, k)
         if workspace is None:
             workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=h.device)

@@ -795,6 +795,210 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
   }
 }
 
+// ---------------------------------------------------------------------------
+// down on the matrix cores for E2M1 rows and BF16 h (expert-major)
+// ---------------------------------------------------------------------------
+//
+// The gate_up ring above with the down product's operands: a wavefront owns
+// (expert, 32 consecutive rows of W_down) as two 16-row MFMA row blocks, the
+// expert's routed entries' h rows are the columns (kMx4Tc per pass), and it
+// writes w * dot for each (entry, row) to the FP32 slot buffer, which the
+// combine kernel then sums in slot order.  Each value is an exact-product FP32
+// accumulation over K in a fixed order that does not depend on the other
+// columns, so y does not depend on the batch; the order differs from the
+// vector kernels' (which stay bit-identical to each other).
+constexpr int kMx4DnLds = kMx4Lds + 4 * kDecodeMaxEntries;   // + the entries' routing weights
+static_assert(kMx4DnLds <= 160 * 1024, "LDS budget");
+
+// Shapes it takes: whole 32-row groups and whole 128-byte row slices.
+bool down_mx4_mfma_fits(const moe_weights& W) {
+  return W.format == W_MXFP4 && W.hidden % 32 == 0 && W.inter % 256 == 0;
+}
+
+__global__ __launch_bounds__(kBlock) void down_mx4_mfma_kernel(const DownArgs a) {
+  constexpr int kRing = kWavesPerBlock * kMx4Ns * kMx4Stage;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMx4DnLds];
+  int* s_ids = reinterpret_cast<int*>(lds + kRing);
+  float* s_wts = reinterpret_cast<float*>(lds + kRing + 4 * kDecodeMaxEntries);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + kRing + 8 * kDecodeMaxEntries);
+  int* s_lists = reinterpret_cast<int*>(lds + kRing + 8 * kDecodeMaxEntries + 4 * kMaskWords);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = wave_in_block();
+  // the routing weights go to LDS with the ids: a global load inside the loop
+  // would wait for every stage in flight (loads complete in issue order)
+  for (int v = threadIdx.x; v < a.n_entries; v += blockDim.x) s_wts[v] = slot_weight(a, v);
+  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
+  const int n_rg = a.H >> 5;
+  const int n_units = U * n_rg;
+  // each wavefront takes a contiguous range of units (consecutive units mostly
+  // share the expert and its entry list, and read adjacent rows)
+  const long long gw = (long long)blockIdx.x * kWavesPerBlock + wv;
+  const long long nw = (long long)gridDim.x * kWavesPerBlock;
+  const int u_first = (int)(gw * n_units / nw), u_end = (int)((gw + 1) * n_units / nw);
+  if (u_first >= u_end) return;
+  const int S = a.row_bytes / kMx4SliceBytes;
+  const int n = lane & 15, g = lane >> 4;
+  const int scale_len = a.I >> 5;
+  int* list_i = s_lists + wv * 2 * kMx4Tc;
+  int* list_c = list_i + kMx4Tc;
+  uint8_t* const ring = lds + wv * kMx4Ns * kMx4Stage;
+  const uint8_t* h8 = reinterpret_cast<const uint8_t*>(a.h);
+  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(a.w2s);
+
+  // rows: load j fills stage rows 8j .. 8j+7, lane -> row 8j + lane/8, LDS
+  // slot lane%8 holding chunk (lane%8) ^ swz(row); scales: lane -> row lane/2,
+  // dword lane%2 of the row's 8 scale bytes of the slice
+  uint32_t w_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    w_off[j] = (uint32_t)r * a.row_bytes + 16u * (uint32_t)((lane & 7) ^ mx4_swz(r));
+  }
+  const int s_row = lane >> 1, s_dw = lane & 1;
+
+  // ---- load cursor: unit (expert rank, 32-row group), pass, stage ----
+  int iu = u_first, ipass = 0, is = 0, icnt = 0, ie = 0, irank = -1;
+  bool idone = false;
+  const uint8_t* iw = nullptr;
+  const uint8_t* i_scale = nullptr;
+  const uint8_t* ih[kMx4XInstr];
+  // h: load j, lane -> entry slot t = (64j + lane) / 32, piece p = lane % 32 of
+  // its 512-byte slice, stored at piece slot p, holding piece p ^ (t % 16)
+  auto load_pass_entries = [&]() {
+    const int have = icnt - kMx4Tc * ipass;
+#pragma unroll
+    for (int j = 0; j < kMx4XInstr; ++j) {
+      const int idx = 64 * j + lane;
+      const int t = idx >> 5, p = idx & 31;
+      const int pe = list_i[t < have ? t : 0];
+      ih[j] = h8 + (size_t)pe * a.I * 2 + 16 * (p ^ (t & 15));
+    }
+  };
+  auto load_unit = [&]() {
+    const int rank = iu / n_rg;
+    const int d0 = (iu - rank * n_rg) * 32;
+    const bool relist = rank != irank || icnt > kMx4Tc;
+    if (rank != irank) ie = select_rank(s_mask, a.n_words, rank);
+    irank = rank;
+    iw = a.w2 + ((size_t)ie * a.H + d0) * a.row_bytes;
+    i_scale = s8 + ((size_t)ie * a.H + d0 + s_row) * scale_len + 4 * s_dw;
+    if (relist) {
+      icnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
+      load_pass_entries();
+    }
+  };
+  load_unit();
+
+  // Every call issues kMx4Ops loads (after the last stage the cursor stays put
+  // and the loads repeat its addresses), so the waits below are exact.
+  auto issue = [&](int q) {
+    const uint32_t so = (uint32_t)is * kMx4SliceBytes;
+    uint8_t* dst = ring + q * kMx4Stage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16_lds(iw + so + w_off[j], dst + 1024 * j);
+#pragma unroll
+    for (int j = 0; j < kMx4XInstr; ++j)
+      dma16_lds(ih[j] + (size_t)is * kMx4XBytes, dst + kMx4X + 1024 * j);
+    dma4_lds(i_scale + 8 * is, dst + kMx4S);
+    asm volatile("" ::: "memory");
+    if (!idone && ++is == S) {
+      is = 0;
+      if (kMx4Tc * (++ipass) < icnt) {
+        pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
+        load_pass_entries();
+      } else if (iu + 1 < u_end) {
+        ipass = 0;
+        ++iu;
+        load_unit();
+      } else {
+        idone = true;
+        is = S - 1;
+      }
+    }
+  };
+
+  // ---- compute cursor ----
+  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cd0 = 0, ce = 0, crank = -1;
+  auto compute_unit = [&]() {
+    const int rank = cu / n_rg;
+    cd0 = (cu - rank * n_rg) * 32;
+    const bool relist = rank != crank || ccnt > kMx4Tc;
+    if (rank != crank) ce = select_rank(s_mask, a.n_words, rank);
+    crank = rank;
+    if (relist) ccnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
+  };
+  compute_unit();
+
+#pragma unroll
+  for (int q = 0; q < kMx4Ns - 1; ++q) issue(q);
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int xt = n % kMx4Tc;   // entry slot of this lane's column (columns >= kMx4Tc repeat)
+  float* out = reinterpret_cast<float*>(a.y);
+  bool cdone = false;
+  while (!cdone) {
+#pragma unroll
+    for (int q = 0; q < kMx4Ns; ++q) {
+      if (cdone) break;
+      wait_vmem_and_lds<(kMx4Ns - 2) * kMx4Ops>();
+      issue((q + kMx4Ns - 1) % kMx4Ns);
+      const uint8_t* st = ring + q * kMx4Stage;
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kMx4S);
+      const uint8_t* hrow = st + kMx4X + xt * kMx4XBytes;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {            // rows 0-15, then rows 16-31 of the unit
+        const int row = 16 * p + n;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int c = 4 * jj + g;            // 16-byte chunk: K 32c .. 32c+31 of the slice
+          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * kMx4SliceBytes +
+                                                          16 * (c ^ mx4_swz(row)));
+          const float scl = e8m0_to_f32((sc[2 * row + (c >> 2)] >> (8 * (c & 3))) & 0xffu);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {        // dword i: K 32c + 8i .. 32c + 8i + 7
+            const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 0);
+            const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 1);
+            const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 2);
+            const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 3);
+            const bf16x8 av = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            const int piece = 4 * c + i;
+            const bf16x8 hv = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(hrow + 16 * (piece ^ (xt & 15))));
+            if (p == 0) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc0, 0, 0, 0);
+            else acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc1, 0, 0, 0);
+          }
+        }
+      }
+      if (++cs == S) {
+        // lane (n, g) holds rows 4g .. 4g+3 of each row block for column n
+        cs = 0;
+        const int have = ccnt - kMx4Tc * cpass;
+        if (n < have && n < kMx4Tc) {
+          const int pe = list_c[n];
+          const float wt = s_wts[pe];
+          float* o = out + (size_t)pe * a.H + cd0 + 4 * g;
+          *reinterpret_cast<float4*>(o) = make_float4(__fmul_rn(acc0[0], wt), __fmul_rn(acc0[1], wt),
+                                                      __fmul_rn(acc0[2], wt), __fmul_rn(acc0[3], wt));
+          *reinterpret_cast<float4*>(o + 16) = make_float4(__fmul_rn(acc1[0], wt), __fmul_rn(acc1[1], wt),
+                                                           __fmul_rn(acc1[2], wt), __fmul_rn(acc1[3], wt));
+        }
+        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kMx4Tc * (++cpass) < ccnt) {
+          pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
+        } else if (cu + 1 < u_end) {
+          cpass = 0;
+          ++cu;
+          compute_unit();
+        } else {
+          cdone = true;
+        }
+      }
+    }
+  }
+  wait_vmem_and_lds<0>();   // no direct-to-LDS load may land after the wavefront ends
+}
+
 // Token-major: y[t][d] = sum over slots j (in order) of w_tj * dot(Wd[e_tj][d], h[t][j]).
 // A workgroup owns one (token, output group); its 4 wavefronts take the slots
 // j = w, w+4, ... and park w * dot in LDS; wavefront 0 adds them in slot order.
@@ -1145,15 +1349,19 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
 
 }  // namespace
 
-// Token-major up to 16 tokens, expert-major beyond (and within the entries
-// it stages).  Measured on the Qwen3-style layer (down alone, MI355X): B = 4,
-// 8, 16: 13.1 / 22.6 / 36.7 us token-major against 17.4 / 27.0 / 38.1
-// expert-major; B = 32: 59.4 against 53.8 (the expert-major rows are read
-// once for all the tokens routed to them; the token-major ones once per
-// (token, slot), from L2 after the first).
+// AUTO: token-major up to 16 tokens, expert-major beyond (and within the
+// entries it stages).  Measured on the Qwen3-style layer (down alone,
+// MI355X): B = 4, 8, 16: 13.1 / 22.6 / 36.7 us token-major against 17.4 /
+// 27.0 / 38.1 expert-major; B = 32: 59.4 against 53.8 (the expert-major rows
+// are read once for all the tokens routed to them; the token-major ones once
+// per (token, slot), from L2 after the first).  MXFP4 rows that fit the
+// matrix-core kernel take expert-major at every batch size, so that a token's
+// y does not change with the batch size there either.
 int down_variant_for(const moe_weights& W, int T, int k) {
   const long long entries = (long long)T * (k + W.num_shared);
-  return T > 16 && entries <= kDecodeMaxEntries ? kDownExpertMajor : kDownTokenMajor;
+  if (entries > kDecodeMaxEntries) return kDownTokenMajor;
+  if (down_mx4_mfma_fits(W)) return kDownExpertMajor;
+  return T > 16 ? kDownExpertMajor : kDownTokenMajor;
 }
 
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
@@ -1177,8 +1385,14 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                 : down_shape<W_MXFP8, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     case W_MXFP4:
-      err = hbf ? down_shape<W_MXFP4, true>(a, p.lpr, em, ybf, p.blocks, s)
-                : down_shape<W_MXFP4, false>(a, p.lpr, em, ybf, p.blocks, s);
+      if (hbf && em == kDownExpertMajor && down_mx4_mfma_fits(W)) {
+        // one persistent workgroup per CU (the stage ring takes most of the LDS)
+        hipLaunchKernelGGL(down_mx4_mfma_kernel, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
+        err = hipGetLastError();
+      } else {
+        err = hbf ? down_shape<W_MXFP4, true>(a, p.lpr, em, ybf, p.blocks, s)
+                  : down_shape<W_MXFP4, false>(a, p.lpr, em, ybf, p.blocks, s);
+      }
       break;
     case W_FP8B128:
       err = hbf ? down_shape<W_FP8B128, true>(a, p.lpr, em, ybf, p.blocks, s)

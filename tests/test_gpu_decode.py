@@ -101,8 +101,7 @@ def test_batch_invariance_and_determinism(lib, fmt):
     assert torch.equal(h_all, h_again) and torch.equal(y_all, y_again)
     for t in (0, 13, 31):
         h1 = lib.gate_up(Wd, xd[t:t + 1].contiguous(), idd[t:t + 1].contiguous())
-        y1 = lib.down(Wd, h1, idd[t:t + 1].contiguous(), wd[t:t + 1].contiguous(),
-                      variant="token")
+        y1 = lib.down(Wd, h1, idd[t:t + 1].contiguous(), wd[t:t + 1].contiguous())
         torch.cuda.synchronize()
         assert torch.equal(h1[0], h_all[t]) and torch.equal(y1[0], y_all[t]), t
 
@@ -111,7 +110,9 @@ def test_batch_invariance_and_determinism(lib, fmt):
 @pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
 def test_down_variants_bitwise_identical(lib, fmt, h_dtype):
     """Token-major and expert-major down give the same bits (same per-slot
-    lane groups and reduction tree, slots added in slot order)."""
+    lane groups and reduction tree, slots added in slot order) -- except
+    MXFP4 rows with BF16 h, whose expert-major down runs on the matrix cores:
+    the same exact products summed in another FP32 order."""
     cfg = SMALL[fmt]
     if fmt == "f32" and h_dtype == "bf16":
         pytest.skip("FP32 weights take an FP32 h")
@@ -125,7 +126,12 @@ def test_down_variants_bitwise_identical(lib, fmt, h_dtype):
         y_exp = torch.full_like(y_tok, float("nan"))
         lib.down(Wd, h, idd, wd, y=y_exp, variant="expert")
         torch.cuda.synchronize()
-        assert torch.equal(y_tok, y_exp), (fmt, y_dtype, "expert")
+        if fmt == "mxfp4" and h_dtype == "bf16":
+            a_, b_ = to_f64(y_tok), to_f64(y_exp)
+            tol = 1e-5 if y_dtype == "f32" else 8e-3   # BF16 y: one rounding of either sum
+            assert np.linalg.norm(a_ - b_) <= tol * np.linalg.norm(a_), (fmt, y_dtype)
+        else:
+            assert torch.equal(y_tok, y_exp), (fmt, y_dtype, "expert")
 
 
 def test_expert_major_down_at_the_entry_limit(lib):
