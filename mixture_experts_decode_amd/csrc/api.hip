@@ -105,6 +105,10 @@ double expert_bytes(const moe_weights* W) {
 //  decode : the touched experts' bytes at 5.9 TB/s and VALU work of
 //           1.45e-7 us per (token, slot) entry per H*I overlap, with half of
 //           the smaller of the two showing through, plus 4 us;
+//           For E2M1 weights both decode kernels run on the matrix cores
+//           and stream an expert's rows once per pass of up to 2, 8 or 12
+//           entries: the expected passes times an expert's bytes at
+//           4.4 TB/s, plus 0.03 us per entry and 14 us.
 //  grouped: the same bytes at 5.2 TB/s (4.0 TB/s for E2M1 weights, whose
 //           stage rows are half cache lines) with the matrix work hidden,
 //           plus 25 us for sort, quantisation, combine and launches.
@@ -117,9 +121,15 @@ int32_t model_path(const moe_weights* W, int32_t T, int32_t k) {
   const double u = n * (1.0 - std::pow(1.0 - p, (double)T)) + W->num_shared;
   const double bytes = u * expert_bytes(W);
   const double entries = (double)T * (k + W->num_shared);
-  const double valu = entries * W->hidden * W->inter * 1.45e-7;
-  const double mem_d = bytes / 5.9e6;
-  const double t_dec = std::max(mem_d, valu) + 0.5 * std::min(mem_d, valu) + 4.0;
+  double t_dec;
+  if (moe::decode_on_matrix_cores(*W)) {
+    t_dec = moe::decode_matrix_core_passes(*W, T, k) * expert_bytes(W) / 4.4e6 + 0.03 * entries +
+            14.0;
+  } else {
+    const double valu = entries * W->hidden * W->inter * 1.45e-7;
+    const double mem_d = bytes / 5.9e6;
+    t_dec = std::max(mem_d, valu) + 0.5 * std::min(mem_d, valu) + 4.0;
+  }
   const double t_grp = bytes / (W->format == MOE_W_MXFP4 ? 4.0e6 : 5.2e6) + 25.0;
   return t_grp < t_dec ? MOE_PATH_GROUPED : MOE_PATH_DECODE;
 }

@@ -29,7 +29,8 @@
 //  * MXFP4 gate_up (E2M1 rows, BF16 activations) runs on the matrix cores
 //    instead: a wavefront owns (expert, 16 neurons) with the expert's routed
 //    entries as MFMA columns, and streams 128-byte row slices through an LDS
-//    ring by direct-to-LDS loads (see gate_up_mx4_mfma_kernel).
+//    ring by direct-to-LDS loads; MXFP4 expert-major down likewise (see
+//    mx4_mfma_kernel).
 //  * 16-byte loads per lane; E4M3 / E2M1 are converted exactly to BF16 and
 //    multiplied with BF16 activations by v_dot2_f32_bf16, or converted to FP32
 //    for FP32 intermediates; the MX / tile scale multiplies each 16-byte
@@ -37,6 +38,7 @@
 //    where an MX scale (a power of two) enters the conversion itself.
 
 #include <algorithm>
+#include <cmath>
 
 #include "device.h"
 #include "internal.h"
@@ -397,287 +399,6 @@ MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs 
 }
 
 // ---------------------------------------------------------------------------
-// gate_up on the matrix cores for E2M1 rows and BF16 activations
-// ---------------------------------------------------------------------------
-//
-// The vector kernel converts E2M1 rows again for every routed token (BF16
-// copies of its rows do not fit in registers), so its work grows with the
-// tokens per expert.  Here a wavefront owns (expert, 16 neurons): their 16
-// gate and 16 up rows are the MFMA row operand, and the expert's routed
-// (token, slot) entries are the column operand of v_mfma_f32_16x16x32_bf16,
-// kMx4Tc at a time (an expert with more entries takes several passes).
-// The rows are cut into 128-byte slices (256 K values).  A slice of the 32
-// rows, the activations of the pass's tokens over the same K range and the
-// rows' E8M0 scales travel HBM -> LDS by direct-to-LDS loads into a ring of
-// kMx4Ns stages per wavefront, so kMx4Ns - 1 stages are in flight while one
-// is consumed and no registers hold staged data.  Each slice is converted to
-// BF16 once (the MX scale, a power of two, enters the conversion exactly)
-// and serves every column.  A lane's A and B operands take the same K values
-// in the same order (a permutation of K that keeps each 16-byte chunk in one
-// lane), so each column is an exact-product FP32 accumulation over K in a
-// fixed order that does not depend on the other columns: h does not depend
-// on the batch.
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kMx4SliceBytes = 128;            // bytes of a row per stage (256 K values)
-constexpr int kMx4Tc = 8;                      // entries (MFMA columns) per pass
-constexpr int kMx4Ns = 4;                      // ring stages per wavefront
-constexpr int kMx4XBytes = 2 * 2 * kMx4SliceBytes;   // BF16 activations per token per stage
-// Stage: W [32 rows][128 B] (16-byte chunks XOR-swizzled by row) |
-//        X [kMx4Tc tokens][512 B] (16-byte pieces XOR-swizzled by token) |
-//        S [32 rows][2 dwords] (the eight E8M0 scales of the row's slice)
-constexpr int kMx4X = 32 * kMx4SliceBytes, kMx4S = kMx4X + kMx4Tc * kMx4XBytes;
-constexpr int kMx4Stage = kMx4S + 256;
-constexpr int kMx4XInstr = kMx4Tc * kMx4XBytes / 1024;
-constexpr int kMx4Ops = 4 + kMx4XInstr + 1;    // direct-to-LDS loads per stage
-static_assert((kMx4Ns - 2) * kMx4Ops < 64, "vmcnt range");
-constexpr int kMx4Lds = kWavesPerBlock * kMx4Ns * kMx4Stage + 4 * kDecodeMaxEntries +
-                        4 * kMaskWords + 4 * kWavesPerBlock * 2 * kMx4Tc;
-static_assert(kMx4Lds <= 160 * 1024, "LDS budget");
-
-__device__ __forceinline__ void dma16_lds(const void* src, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4_lds(const void* src, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
-}
-// Until at most N vector-memory operations of this wavefront are outstanding
-// (they complete in issue order) and all its LDS reads have returned.
-template <int N>
-__device__ __forceinline__ void wait_vmem_and_lds() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-  asm volatile("" ::: "memory");
-}
-// LDS slot of 16-byte chunk c of row r inside a 128-byte slice: a bijection
-// per row under which 16 consecutive rows reading one chunk hit distinct banks.
-__device__ __forceinline__ int mx4_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// Entries of expert e with rank [TC * pass, TC * (pass + 1)) in entry order
-// -> list[0 .. TC); returns the number of entries of e.  Whole wavefront.
-template <int TC>
-__device__ __forceinline__ int pass_entries(const int* s_ids, int n_entries, int e, int pass,
-                                            int* list) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int seen = 0;
-  for (int b = 0; b < n_entries; b += kWave) {
-    const int v = b + lane;
-    const bool m = v < n_entries && s_ids[v] == e;
-    const unsigned long long bm = __ballot(m);
-    if (m) {
-      const int r = seen + __popcll(bm & ((1ull << lane) - 1ull)) - TC * pass;
-      if (r >= 0 && r < TC) list[r] = v;
-    }
-    seen += __popcll(bm);
-  }
-  return seen;
-}
-
-// Shapes the matrix-core kernel takes: whole 16-neuron blocks and whole
-// 128-byte row slices (I % 16 == 0, H % 256 == 0).
-bool gate_up_mx4_mfma_fits(const moe_weights& W) {
-  return W.inter % 16 == 0 && W.hidden % 256 == 0;
-}
-
-template <bool HBF16>
-__global__ __launch_bounds__(kBlock) void gate_up_mx4_mfma_kernel(const GateUpArgs a) {
-  constexpr int kRing = kWavesPerBlock * kMx4Ns * kMx4Stage;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMx4Lds];
-  // one LDS array: the compiler then orders LDS reads against the
-  // direct-to-LDS loads only through the explicit waits below
-  int* s_ids = reinterpret_cast<int*>(lds + kRing);
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + kRing + 4 * kDecodeMaxEntries);
-  int* s_lists = reinterpret_cast<int*>(lds + kRing + 4 * kDecodeMaxEntries + 4 * kMaskWords);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = wave_in_block();
-  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
-  const int n_nb = a.I >> 4;
-  const int n_units = U * n_nb;
-  // each wavefront takes a contiguous range of units, so consecutive units
-  // mostly share the expert (and its entry list) and read adjacent rows
-  const long long gw = (long long)blockIdx.x * kWavesPerBlock + wv;
-  const long long nw = (long long)gridDim.x * kWavesPerBlock;
-  const int u_first = (int)(gw * n_units / nw), u_end = (int)((gw + 1) * n_units / nw);
-  if (u_first >= u_end) return;
-  const int S = a.row_bytes / kMx4SliceBytes;   // stages per pass
-  const int n = lane & 15, g = lane >> 4;       // MFMA column / K group of this lane
-  const int scale_row = a.H >> 5;               // E8M0 bytes per row
-  int* list_i = s_lists + wv * 2 * kMx4Tc;      // entries of the pass being loaded
-  int* list_c = list_i + kMx4Tc;                // entries of the pass being computed
-  uint8_t* const ring = lds + wv * kMx4Ns * kMx4Stage;
-  const uint8_t* x8 = reinterpret_cast<const uint8_t*>(a.x);
-  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(a.w13s);
-
-  // Per-lane source offsets, fixed for the whole kernel.  Weights: load j
-  // fills stage rows 8j .. 8j+7 (rows 0-15 gate, 16-31 up), lane -> row
-  // 8j + lane/8, LDS slot lane%8 holding chunk (lane%8) ^ swz(row).
-  uint32_t w_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * j + (lane >> 3);
-    w_off[j] = (uint32_t)(r & 15) * a.row_bytes + 16u * (uint32_t)((lane & 7) ^ mx4_swz(r));
-  }
-  // scales: lane -> row lane/2, dword lane%2 of the row's 8 scale bytes
-  const int s_row = lane >> 1, s_dw = lane & 1;
-
-  // ---- load cursor: unit (expert rank, neuron block), pass, stage ----
-  int iu = u_first, ipass = 0, is = 0, icnt = 0, ie = 0;
-  bool idone = false;
-  const uint8_t* iw_gate = nullptr;
-  const uint8_t* iw_up = nullptr;
-  const uint8_t* i_scale = nullptr;
-  const uint8_t* ix[kMx4XInstr];
-  // activations: load j, lane -> token slot t = (64j + lane) / 32, piece
-  // p = lane % 32 of its 512-byte slice, stored at piece slot p, holding
-  // piece p ^ (t % 16)
-  auto load_pass_tokens = [&]() {
-    const int have = icnt - kMx4Tc * ipass;
-#pragma unroll
-    for (int j = 0; j < kMx4XInstr; ++j) {
-      const int idx = 64 * j + lane;
-      const int t = idx >> 5, p = idx & 31;
-      const int pe = list_i[t < have ? t : 0];
-      ix[j] = x8 + (size_t)div_slots(pe, a.slots_magic) * a.H * 2 + 16 * (p ^ (t & 15));
-    }
-  };
-  int irank = -1;
-  auto load_unit = [&]() {
-    const int rank = iu / n_nb;
-    const int nb = iu - rank * n_nb;
-    // a new expert, or one whose entries took several passes: find pass 0
-    const bool relist = rank != irank || icnt > kMx4Tc;
-    if (rank != irank) ie = select_rank(s_mask, a.n_words, rank);
-    irank = rank;
-    const long long r0 = (long long)ie * 2 * a.I + nb * 16;
-    iw_gate = a.w13 + r0 * a.row_bytes;
-    iw_up = a.w13 + (r0 + a.I) * a.row_bytes;
-    i_scale = s8 + (r0 + (s_row >> 4) * (long long)a.I + (s_row & 15)) * scale_row + 4 * s_dw;
-    if (relist) {
-      icnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
-      load_pass_tokens();
-    }
-  };
-  load_unit();
-
-  // Every call issues kMx4Ops loads: after the last stage the cursor stays
-  // put and the loads repeat its addresses (in L2), so the waits are exact.
-  auto issue = [&](int q) {
-    const uint32_t so = (uint32_t)is * kMx4SliceBytes;
-    uint8_t* dst = ring + q * kMx4Stage;
-    dma16_lds(iw_gate + so + w_off[0], dst);
-    dma16_lds(iw_gate + so + w_off[1], dst + 1024);
-    dma16_lds(iw_up + so + w_off[2], dst + 2048);
-    dma16_lds(iw_up + so + w_off[3], dst + 3072);
-#pragma unroll
-    for (int j = 0; j < kMx4XInstr; ++j)
-      dma16_lds(ix[j] + (size_t)is * kMx4XBytes, dst + kMx4X + 1024 * j);
-    dma4_lds(i_scale + 8 * is, dst + kMx4S);
-    asm volatile("" ::: "memory");
-    if (!idone && ++is == S) {
-      is = 0;
-      if (kMx4Tc * (++ipass) < icnt) {
-        pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
-        load_pass_tokens();
-      } else if (iu + 1 < u_end) {
-        ipass = 0;
-        ++iu;
-        load_unit();
-      } else {
-        idone = true;
-        is = S - 1;
-      }
-    }
-  };
-
-  // ---- compute cursor ----
-  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cnb = 0, ce = 0, crank = -1;
-  auto compute_unit = [&]() {
-    const int rank = cu / n_nb;
-    cnb = cu - rank * n_nb;
-    const bool relist = rank != crank || ccnt > kMx4Tc;
-    if (rank != crank) ce = select_rank(s_mask, a.n_words, rank);
-    crank = rank;
-    if (relist) ccnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
-  };
-  compute_unit();
-
-#pragma unroll
-  for (int q = 0; q < kMx4Ns - 1; ++q) issue(q);
-
-  f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
-  const int xt = n % kMx4Tc;   // token slot of this lane's column (columns >= kMx4Tc repeat)
-  bool cdone = false;
-  while (!cdone) {
-#pragma unroll
-    for (int q = 0; q < kMx4Ns; ++q) {
-      if (cdone) break;
-      wait_vmem_and_lds<(kMx4Ns - 2) * kMx4Ops>();
-      issue((q + kMx4Ns - 1) % kMx4Ns);
-      const uint8_t* st = ring + q * kMx4Stage;
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kMx4S);
-      const uint8_t* xrow = st + kMx4X + xt * kMx4XBytes;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {            // gate rows, then up rows
-        const int row = 16 * p + n;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int c = 4 * jj + g;            // 16-byte chunk: K 32c .. 32c+31 of the slice
-          const u32x4 w = *reinterpret_cast<const u32x4*>(st + row * kMx4SliceBytes +
-                                                          16 * (c ^ mx4_swz(row)));
-          const float scl = e8m0_to_f32((sc[2 * row + (c >> 2)] >> (8 * (c & 3))) & 0xffu);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {        // dword i: K 32c + 8i .. 32c + 8i + 7
-            const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 0);
-            const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 1);
-            const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 2);
-            const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 3);
-            const bf16x8 av = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-            const int piece = 4 * c + i;
-            const bf16x8 xv = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(xrow + 16 * (piece ^ (xt & 15))));
-            if (p == 0) acc_g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc_g, 0, 0, 0);
-            else acc_u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc_u, 0, 0, 0);
-          }
-        }
-      }
-      if (++cs == S) {
-        // lane (n, g) holds neurons 4g .. 4g+3 of the block for column n
-        cs = 0;
-        const int have = ccnt - kMx4Tc * cpass;
-        if (n < have && n < kMx4Tc) {
-          const size_t off = (size_t)list_c[n] * a.I + cnb * 16 + 4 * g;
-          float o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = swiglu(acc_g[i], acc_u[i]);
-          if constexpr (HBF16) {
-            const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + off) = make_uint2(lo, hi);
-          } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.h) + off) =
-                make_float4(o[0], o[1], o[2], o[3]);
-          }
-        }
-        acc_g = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc_u = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kMx4Tc * (++cpass) < ccnt) {
-          pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
-        } else if (cu + 1 < u_end) {
-          cpass = 0;
-          ++cu;
-          compute_unit();
-        } else {
-          cdone = true;
-        }
-      }
-    }
-  }
-  wait_vmem_and_lds<0>();   // no direct-to-LDS load may land after the wavefront ends
-}
-
-// ---------------------------------------------------------------------------
 // down: shared per-row dot product over LPR lanes
 // ---------------------------------------------------------------------------
 
@@ -796,120 +517,275 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
 }
 
 // ---------------------------------------------------------------------------
-// down on the matrix cores for E2M1 rows and BF16 h (expert-major)
+// gate_up and down on the matrix cores for E2M1 rows and BF16 activations
 // ---------------------------------------------------------------------------
 //
-// The gate_up ring above with the down product's operands: a wavefront owns
-// (expert, 32 consecutive rows of W_down) as two 16-row MFMA row blocks, the
-// expert's routed entries' h rows are the columns (kMx4Tc per pass), and it
-// writes w * dot for each (entry, row) to the FP32 slot buffer, which the
-// combine kernel then sums in slot order.  Each value is an exact-product FP32
-// accumulation over K in a fixed order that does not depend on the other
-// columns, so y does not depend on the batch; the order differs from the
-// vector kernels' (which stay bit-identical to each other).
-constexpr int kMx4DnLds = kMx4Lds + 4 * kDecodeMaxEntries;   // + the entries' routing weights
-static_assert(kMx4DnLds <= 160 * 1024, "LDS budget");
+// With E2M1 rows the vector kernels convert every row again for each routed
+// token (BF16 copies of the rows do not fit in registers), so their work grows
+// with the tokens per expert.  These kernels put the rows on the matrix
+// cores instead.  A wavefront owns a unit: 32 weight rows of one expert (the
+// gate and up rows of 16 neurons, or 32 consecutive rows of W_down), as two
+// 16-row operand blocks of v_mfma_f32_16x16x32_bf16, against up to TC of the
+// expert's routed entries as the columns.  An expert with more than TC entries
+// is split into "virtual experts" (passes of TC entries), each a separate run
+// of units, so a heavily routed expert is spread over many wavefronts.  Units
+// are dealt to the wavefronts in contiguous ranges (consecutive units share
+// the expert and its entry list, and read adjacent rows).
+// The rows are cut into 128-byte slices (256 K values).  A slice of the 32
+// rows, the columns' BF16 activations over the same K range and the rows'
+// E8M0 scales travel HBM -> LDS by direct-to-LDS loads into a ring of NS
+// stages per wavefront: NS - 1 stages are in flight while one is consumed,
+// and no registers hold staged data.  Each slice is converted to BF16 once
+// (the MX scale, a power of two, enters the conversion exactly) and feeds
+// every column.  A lane's A and B operands take the same K values in the same
+// order (a permutation of K that keeps each 16-byte chunk in one lane), so
+// each column is an exact-product FP32 accumulation over K in a fixed order
+// that depends neither on the other columns nor on TC or NS: results do not
+// depend on the batch (tested bitwise).
+//   gate_up: h[pe][n] = SiLU(gate . x) * (up . x), x the entry's token row.
+//   down:    slot_out[pe][d] = w_pe * (Wd[d] . h[pe]), summed in slot order
+//            by the combine kernel.
 
-// Shapes it takes: whole 32-row groups and whole 128-byte row slices.
-bool down_mx4_mfma_fits(const moe_weights& W) {
-  return W.format == W_MXFP4 && W.hidden % 32 == 0 && W.inter % 256 == 0;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMx4SliceBytes = 128;   // bytes of a row per stage (256 K values)
+constexpr int kMx4XBytes = 512;       // BF16 activations of one column per stage
+
+struct Mx4Args {
+  const uint8_t* w;       // gate_up: w13 [E+S][2I][H/2]; down: w2 [E+S][H][I/2]
+  const uint8_t* ws;      // E8M0 scales, K/32 per row
+  const uint8_t* act;     // gate_up: x [T][H]; down: h [T*slots][I] (BF16)
+  const int32_t* ids;
+  const float* wts;       // down only
+  void* out;              // gate_up: h [T*slots][I]; down: slot_out [T*slots][H] FP32
+  int T, k, slots, E, n_words, n_entries;
+  int K, N;               // reduction length; gate_up: neurons I, down: rows H
+  int row_bytes;          // K / 2
+  int n_groups;           // units per virtual expert: I / 16 or H / 32
+  uint32_t slots_magic;
+};
+
+// LDS layout of one instantiation: the ring, then the work map.
+template <int TC, int NS, bool DOWN>
+struct Mx4Lds {
+  static constexpr int X = 32 * kMx4SliceBytes;        // stage: W [32 rows][128 B] (chunks
+  static constexpr int S = X + TC * kMx4XBytes;        //  swizzled by row) | X [TC][512 B]
+  static constexpr int STAGE = S + 256;                //  (pieces swizzled by column) | S
+  static constexpr int XI = TC * kMx4XBytes / 1024;    // activation loads per stage
+  static constexpr int OPS = 4 + XI + 1;               // direct-to-LDS loads per stage
+  static constexpr int RING = kWavesPerBlock * NS * STAGE;
+  static constexpr int IDS = RING;                                  // int16 [entries]
+  static constexpr int CNT = IDS + 2 * kDecodeMaxEntries;           // int32 [experts]
+  static constexpr int REXP = CNT + 4 * kMaxExpertsTotal;           // int16 [experts]
+  static constexpr int VSTART = REXP + 2 * kMaxExpertsTotal;        // int16 [experts + 1]
+  static constexpr int MASK = VSTART + 2 * kMaxExpertsTotal + 16;   // uint32 [words]
+  static constexpr int LISTS = MASK + 4 * kMaskWords;               // int32 [waves][2][TC]
+  static constexpr int WTS = LISTS + 4 * kWavesPerBlock * 2 * TC;   // float [entries] (down)
+  static constexpr int TOT = WTS + (DOWN ? 4 * kDecodeMaxEntries : 0);
+  static constexpr int BYTES = TOT + 16;
+  static_assert(XI >= 1 && TC * kMx4XBytes % 1024 == 0, "whole activation loads");
+  static_assert(TC <= 16, "at most the MFMA's 16 columns");
+  static_assert((NS - 2) * OPS < 64, "vmcnt range");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ void dma16_lds(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_lds(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// Until at most N vector-memory operations of this wavefront are outstanding
+// (they complete in issue order) and all its LDS reads have returned.
+template <int N>
+__device__ __forceinline__ void wait_vmem_and_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
+// LDS slot of 16-byte chunk c of row r inside a 128-byte slice: a bijection
+// per row under which 16 consecutive rows reading one chunk hit distinct banks.
+__device__ __forceinline__ int mx4_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Entries of expert e with rank [TC * pass, TC * (pass + 1)) in entry order
+// -> list[0 .. TC).  Whole wavefront.
+template <int TC>
+__device__ __forceinline__ void pass_entries(const int16_t* s_ids, int n_entries, int e, int pass,
+                                             int* list) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int seen = 0;
+  for (int b = 0; b < n_entries; b += kWave) {
+    const int v = b + lane;
+    const bool m = v < n_entries && s_ids[v] == e;
+    const unsigned long long bm = __ballot(m);
+    if (m) {
+      const int r = seen + __popcll(bm & ((1ull << lane) - 1ull)) - TC * pass;
+      if (r >= 0 && r < TC) list[r] = v;
+    }
+    seen += __popcll(bm);
+  }
 }
 
-__global__ __launch_bounds__(kBlock) void down_mx4_mfma_kernel(const DownArgs a) {
-  constexpr int kRing = kWavesPerBlock * kMx4Ns * kMx4Stage;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMx4DnLds];
-  int* s_ids = reinterpret_cast<int*>(lds + kRing);
-  float* s_wts = reinterpret_cast<float*>(lds + kRing + 4 * kDecodeMaxEntries);
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + kRing + 8 * kDecodeMaxEntries);
-  int* s_lists = reinterpret_cast<int*>(lds + kRing + 8 * kDecodeMaxEntries + 4 * kMaskWords);
-  const int lane = threadIdx.x & (kWave - 1);
+// Last rank r with vstart[r] <= v (uniform inputs; vstart strictly increases).
+__device__ __forceinline__ int rank_of(const int16_t* vstart, int U, int v) {
+  int lo = 0, hi = U - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (vstart[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int TC, int NS, bool DOWN, bool HBF16>
+__global__ __launch_bounds__(kBlock) void mx4_mfma_kernel(const Mx4Args a) {
+  using L = Mx4Lds<TC, NS, DOWN>;
+  // one LDS array: the compiler then orders LDS reads against the
+  // direct-to-LDS loads only through the explicit waits below
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
+  int16_t* s_ids = reinterpret_cast<int16_t*>(lds + L::IDS);
+  int* s_cnt = reinterpret_cast<int*>(lds + L::CNT);
+  int16_t* s_rexp = reinterpret_cast<int16_t*>(lds + L::REXP);
+  int16_t* s_vstart = reinterpret_cast<int16_t*>(lds + L::VSTART);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + L::MASK);
+  float* s_wts = reinterpret_cast<float*>(lds + L::WTS);
+  int* s_tot = reinterpret_cast<int*>(lds + L::TOT);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = wave_in_block();
-  // the routing weights go to LDS with the ids: a global load inside the loop
-  // would wait for every stage in flight (loads complete in issue order)
-  for (int v = threadIdx.x; v < a.n_entries; v += blockDim.x) s_wts[v] = slot_weight(a, v);
-  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
-  const int n_rg = a.H >> 5;
-  const int n_units = U * n_rg;
-  // each wavefront takes a contiguous range of units (consecutive units mostly
-  // share the expert and its entry list, and read adjacent rows)
+
+  // ---- work map (whole workgroup): entry -> expert, entries per expert, the
+  // touched experts in ascending order and each one's first virtual expert ----
+  const int n_exp = a.n_words * 32;
+  for (int q = tid; q < a.n_words; q += blockDim.x) s_mask[q] = 0;
+  for (int e = tid; e < n_exp; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+  for (int v = tid; v < a.n_entries; v += blockDim.x) {
+    const int t = div_slots(v, a.slots_magic), j = v - t * a.slots;
+    const int e = j < a.k ? clamp_expert(a.ids[t * a.k + j], a.E) : a.E;
+    s_ids[v] = (int16_t)e;
+    atomicOr(&s_mask[e >> 5], 1u << (e & 31));
+    atomicAdd(&s_cnt[e], 1);
+    // routing weights go to LDS too: a global load inside the loop below
+    // would wait for every stage in flight (loads complete in issue order)
+    if constexpr (DOWN) s_wts[v] = j < a.k ? a.wts[t * a.k + j] : 1.0f;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int rank0 = 0, v0 = 0;
+    for (int e0 = 0; e0 < n_exp; e0 += kWave) {
+      const int e = e0 + lane;
+      const bool touched = e < n_exp && ((s_mask[e >> 5] >> (e & 31)) & 1u);
+      const unsigned long long bm = __ballot(touched);
+      const int r = rank0 + __popcll(bm & ((1ull << lane) - 1ull));
+      const int p = touched ? (s_cnt[e] + TC - 1) / TC : 0;
+      int incl = p;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      if (touched) {
+        s_rexp[r] = (int16_t)e;
+        s_vstart[r] = (int16_t)(v0 + incl - p);
+      }
+      v0 += __shfl(incl, kWave - 1, kWave);
+      rank0 += __popcll(bm);
+    }
+    if (lane == 0) {
+      s_vstart[rank0] = (int16_t)v0;
+      s_tot[0] = rank0;
+      s_tot[1] = v0;
+    }
+  }
+  __syncthreads();
+  const int U = s_tot[0];
+  const int n_units = s_tot[1] * a.n_groups;
   const long long gw = (long long)blockIdx.x * kWavesPerBlock + wv;
   const long long nw = (long long)gridDim.x * kWavesPerBlock;
   const int u_first = (int)(gw * n_units / nw), u_end = (int)((gw + 1) * n_units / nw);
   if (u_first >= u_end) return;
-  const int S = a.row_bytes / kMx4SliceBytes;
-  const int n = lane & 15, g = lane >> 4;
-  const int scale_len = a.I >> 5;
-  int* list_i = s_lists + wv * 2 * kMx4Tc;
-  int* list_c = list_i + kMx4Tc;
-  uint8_t* const ring = lds + wv * kMx4Ns * kMx4Stage;
-  const uint8_t* h8 = reinterpret_cast<const uint8_t*>(a.h);
-  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(a.w2s);
 
-  // rows: load j fills stage rows 8j .. 8j+7, lane -> row 8j + lane/8, LDS
-  // slot lane%8 holding chunk (lane%8) ^ swz(row); scales: lane -> row lane/2,
-  // dword lane%2 of the row's 8 scale bytes of the slice
+  const int S = a.row_bytes / kMx4SliceBytes;   // stages per unit
+  const int n = lane & 15, g = lane >> 4;       // MFMA column / K group of this lane
+  const int scale_len = a.K >> 5;               // E8M0 bytes per row
+  int* list_i = reinterpret_cast<int*>(lds + L::LISTS) + wv * 2 * TC;   // columns being loaded
+  int* list_c = list_i + TC;                                            // columns being computed
+  uint8_t* const ring = lds + wv * NS * L::STAGE;
+
+  // Per-lane source offsets, fixed for the whole kernel.  Rows: load j fills
+  // stage rows 8j .. 8j+7 (0-15 the first operand block, 16-31 the second),
+  // lane -> row 8j + lane/8, LDS slot lane%8 holding chunk (lane%8) ^ swz(row).
+  // Scales: lane -> row lane/2, dword lane%2 of the row's 8 bytes of the slice.
   uint32_t w_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * j + (lane >> 3);
-    w_off[j] = (uint32_t)r * a.row_bytes + 16u * (uint32_t)((lane & 7) ^ mx4_swz(r));
+    w_off[j] = (uint32_t)(r & 15) * a.row_bytes + 16u * (uint32_t)((lane & 7) ^ mx4_swz(r));
   }
   const int s_row = lane >> 1, s_dw = lane & 1;
 
-  // ---- load cursor: unit (expert rank, 32-row group), pass, stage ----
-  int iu = u_first, ipass = 0, is = 0, icnt = 0, ie = 0, irank = -1;
-  bool idone = false;
-  const uint8_t* iw = nullptr;
-  const uint8_t* i_scale = nullptr;
-  const uint8_t* ih[kMx4XInstr];
-  // h: load j, lane -> entry slot t = (64j + lane) / 32, piece p = lane % 32 of
-  // its 512-byte slice, stored at piece slot p, holding piece p ^ (t % 16)
-  auto load_pass_entries = [&]() {
-    const int have = icnt - kMx4Tc * ipass;
-#pragma unroll
-    for (int j = 0; j < kMx4XInstr; ++j) {
-      const int idx = 64 * j + lane;
-      const int t = idx >> 5, p = idx & 31;
-      const int pe = list_i[t < have ? t : 0];
-      ih[j] = h8 + (size_t)pe * a.I * 2 + 16 * (p ^ (t & 15));
-    }
+  // a unit's two 16-row blocks of expert e: gate / up rows of neurons
+  // 16 grp .. 16 grp + 15, or rows 32 grp .. 32 grp + 31 of W_down
+  auto row_block = [&](int e, int grp, int blk) -> long long {
+    if constexpr (DOWN) return (long long)e * a.N + 32 * grp + 16 * blk;
+    else return ((long long)e * 2 + blk) * a.N + 16 * grp;
   };
-  auto load_unit = [&]() {
-    const int rank = iu / n_rg;
-    const int d0 = (iu - rank * n_rg) * 32;
-    const bool relist = rank != irank || icnt > kMx4Tc;
-    if (rank != irank) ie = select_rank(s_mask, a.n_words, rank);
-    irank = rank;
-    iw = a.w2 + ((size_t)ie * a.H + d0) * a.row_bytes;
-    i_scale = s8 + ((size_t)ie * a.H + d0 + s_row) * scale_len + 4 * s_dw;
-    if (relist) {
-      icnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
-      load_pass_entries();
-    }
-  };
-  load_unit();
 
-  // Every call issues kMx4Ops loads (after the last stage the cursor stays put
-  // and the loads repeat its addresses), so the waits below are exact.
+  // ---- load cursor ----
+  int iu = u_first, is = 0, iv = -1, ie = 0, ihave = 0;
+  bool idone = false;
+  const uint8_t* iw0 = nullptr;
+  const uint8_t* iw1 = nullptr;
+  const uint8_t* i_scale = nullptr;
+  const uint8_t* ix[L::XI];
+  auto enter_unit_i = [&]() {
+    const int v = iu / a.n_groups, grp = iu - v * a.n_groups;
+    if (v != iv) {   // a new virtual expert: its columns
+      iv = v;
+      const int r = rank_of(s_vstart, U, v);
+      ie = s_rexp[r];
+      const int pass = v - s_vstart[r];
+      ihave = min(s_cnt[ie] - TC * pass, TC);
+      pass_entries<TC>(s_ids, a.n_entries, ie, pass, list_i);
+      // activations: load j, lane -> column t = (64j + lane) / 32, piece
+      // p = lane % 32 of its 512-byte slice, stored at piece slot p holding
+      // piece p ^ (t % 16)
+#pragma unroll
+      for (int j = 0; j < L::XI; ++j) {
+        const int idx = 64 * j + lane;
+        const int t = idx >> 5, p = idx & 31;
+        const int pe = list_i[t < ihave ? t : 0];
+        const int row = DOWN ? pe : div_slots(pe, a.slots_magic);
+        ix[j] = a.act + (size_t)row * a.K * 2 + 16 * (p ^ (t & 15));
+      }
+    }
+    const long long r0 = row_block(ie, grp, 0), r1 = row_block(ie, grp, 1);
+    iw0 = a.w + r0 * a.row_bytes;
+    iw1 = a.w + r1 * a.row_bytes;
+    i_scale = a.ws + ((s_row < 16 ? r0 : r1) + (s_row & 15)) * scale_len + 4 * s_dw;
+  };
+  enter_unit_i();
+
+  // Every call issues L::OPS loads (after the last stage the cursor stays put
+  // and the loads repeat its addresses, which are in L2), so the waits below
+  // are exact.
   auto issue = [&](int q) {
     const uint32_t so = (uint32_t)is * kMx4SliceBytes;
-    uint8_t* dst = ring + q * kMx4Stage;
+    uint8_t* dst = ring + q * L::STAGE;
+    dma16_lds(iw0 + so + w_off[0], dst);
+    dma16_lds(iw0 + so + w_off[1], dst + 1024);
+    dma16_lds(iw1 + so + w_off[2], dst + 2048);
+    dma16_lds(iw1 + so + w_off[3], dst + 3072);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16_lds(iw + so + w_off[j], dst + 1024 * j);
-#pragma unroll
-    for (int j = 0; j < kMx4XInstr; ++j)
-      dma16_lds(ih[j] + (size_t)is * kMx4XBytes, dst + kMx4X + 1024 * j);
-    dma4_lds(i_scale + 8 * is, dst + kMx4S);
+    for (int j = 0; j < L::XI; ++j)
+      dma16_lds(ix[j] + (size_t)is * kMx4XBytes, dst + L::X + 1024 * j);
+    dma4_lds(i_scale + 8 * is, dst + L::S);
     asm volatile("" ::: "memory");
     if (!idone && ++is == S) {
-      is = 0;
-      if (kMx4Tc * (++ipass) < icnt) {
-        pass_entries<kMx4Tc>(s_ids, a.n_entries, ie, ipass, list_i);
-        load_pass_entries();
-      } else if (iu + 1 < u_end) {
-        ipass = 0;
+      if (iu + 1 < u_end) {
+        is = 0;
         ++iu;
-        load_unit();
+        enter_unit_i();
       } else {
         idone = true;
         is = S - 1;
@@ -918,35 +794,38 @@ __global__ __launch_bounds__(kBlock) void down_mx4_mfma_kernel(const DownArgs a)
   };
 
   // ---- compute cursor ----
-  int cu = u_first, cpass = 0, cs = 0, ccnt = 0, cd0 = 0, ce = 0, crank = -1;
-  auto compute_unit = [&]() {
-    const int rank = cu / n_rg;
-    cd0 = (cu - rank * n_rg) * 32;
-    const bool relist = rank != crank || ccnt > kMx4Tc;
-    if (rank != crank) ce = select_rank(s_mask, a.n_words, rank);
-    crank = rank;
-    if (relist) ccnt = pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
+  int cu = u_first, cs = 0, cv = -1, chave = 0, cgrp = 0;
+  auto enter_unit_c = [&]() {
+    const int v = cu / a.n_groups;
+    cgrp = cu - v * a.n_groups;
+    if (v != cv) {
+      cv = v;
+      const int r = rank_of(s_vstart, U, v);
+      const int e = s_rexp[r];
+      const int pass = v - s_vstart[r];
+      chave = min(s_cnt[e] - TC * pass, TC);
+      pass_entries<TC>(s_ids, a.n_entries, e, pass, list_c);
+    }
   };
-  compute_unit();
+  enter_unit_c();
 
 #pragma unroll
-  for (int q = 0; q < kMx4Ns - 1; ++q) issue(q);
+  for (int q = 0; q < NS - 1; ++q) issue(q);
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int xt = n % kMx4Tc;   // entry slot of this lane's column (columns >= kMx4Tc repeat)
-  float* out = reinterpret_cast<float*>(a.y);
+  const int xt = n % TC;   // column slot this lane reads (columns >= TC repeat)
   bool cdone = false;
   while (!cdone) {
 #pragma unroll
-    for (int q = 0; q < kMx4Ns; ++q) {
+    for (int q = 0; q < NS; ++q) {
       if (cdone) break;
-      wait_vmem_and_lds<(kMx4Ns - 2) * kMx4Ops>();
-      issue((q + kMx4Ns - 1) % kMx4Ns);
-      const uint8_t* st = ring + q * kMx4Stage;
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + kMx4S);
-      const uint8_t* hrow = st + kMx4X + xt * kMx4XBytes;
+      wait_vmem_and_lds<(NS - 2) * L::OPS>();
+      issue((q + NS - 1) % NS);
+      const uint8_t* st = ring + q * L::STAGE;
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + L::S);
+      const uint8_t* xrow = st + L::X + xt * kMx4XBytes;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {            // rows 0-15, then rows 16-31 of the unit
+      for (int p = 0; p < 2; ++p) {            // operand blocks: rows 0-15, 16-31
         const int row = 16 * p + n;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -962,34 +841,47 @@ __global__ __launch_bounds__(kBlock) void down_mx4_mfma_kernel(const DownArgs a)
             const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scl, 3);
             const bf16x8 av = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
             const int piece = 4 * c + i;
-            const bf16x8 hv = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(hrow + 16 * (piece ^ (xt & 15))));
-            if (p == 0) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc0, 0, 0, 0);
-            else acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc1, 0, 0, 0);
+            const bf16x8 xv = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(xrow + 16 * (piece ^ (xt & 15))));
+            if (p == 0) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc0, 0, 0, 0);
+            else acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xv, acc1, 0, 0, 0);
           }
         }
       }
       if (++cs == S) {
-        // lane (n, g) holds rows 4g .. 4g+3 of each row block for column n
+        // lane (n, g) holds rows 4g .. 4g+3 of each operand block for column n
         cs = 0;
-        const int have = ccnt - kMx4Tc * cpass;
-        if (n < have && n < kMx4Tc) {
+        if (n < chave) {
           const int pe = list_c[n];
-          const float wt = s_wts[pe];
-          float* o = out + (size_t)pe * a.H + cd0 + 4 * g;
-          *reinterpret_cast<float4*>(o) = make_float4(__fmul_rn(acc0[0], wt), __fmul_rn(acc0[1], wt),
-                                                      __fmul_rn(acc0[2], wt), __fmul_rn(acc0[3], wt));
-          *reinterpret_cast<float4*>(o + 16) = make_float4(__fmul_rn(acc1[0], wt), __fmul_rn(acc1[1], wt),
-                                                           __fmul_rn(acc1[2], wt), __fmul_rn(acc1[3], wt));
+          if constexpr (DOWN) {
+            const float wt = s_wts[pe];
+            float* o = reinterpret_cast<float*>(a.out) + (size_t)pe * a.N + 32 * cgrp + 4 * g;
+            *reinterpret_cast<float4*>(o) =
+                make_float4(__fmul_rn(acc0[0], wt), __fmul_rn(acc0[1], wt),
+                            __fmul_rn(acc0[2], wt), __fmul_rn(acc0[3], wt));
+            *reinterpret_cast<float4*>(o + 16) =
+                make_float4(__fmul_rn(acc1[0], wt), __fmul_rn(acc1[1], wt),
+                            __fmul_rn(acc1[2], wt), __fmul_rn(acc1[3], wt));
+          } else {
+            const size_t off = (size_t)pe * a.N + 16 * cgrp + 4 * g;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = swiglu(acc0[i], acc1[i]);
+            if constexpr (HBF16) {
+              const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+              const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + off) = make_uint2(lo, hi);
+            } else {
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + off) =
+                  make_float4(o[0], o[1], o[2], o[3]);
+            }
+          }
         }
         acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kMx4Tc * (++cpass) < ccnt) {
-          pass_entries<kMx4Tc>(s_ids, a.n_entries, ce, cpass, list_c);
-        } else if (cu + 1 < u_end) {
-          cpass = 0;
+        if (cu + 1 < u_end) {
           ++cu;
-          compute_unit();
+          enter_unit_c();
         } else {
           cdone = true;
         }
@@ -997,6 +889,64 @@ __global__ __launch_bounds__(kBlock) void down_mx4_mfma_kernel(const DownArgs a)
     }
   }
   wait_vmem_and_lds<0>();   // no direct-to-LDS load may land after the wavefront ends
+}
+
+// Shapes they take: whole 16-neuron / 32-row units and whole 128-byte row
+// slices of both matrices.
+bool mx4_mfma_fits(const moe_weights& W) {
+  return W.format == W_MXFP4 && W.inter % 256 == 0 && W.hidden % 256 == 0;
+}
+
+// Columns per pass and ring depth, from the expected entries per touched
+// expert under uniform routing: 2 columns and a 6-stage ring for (nearly) one
+// entry per expert, 8 and 4 up to four (one pass for almost every expert),
+// 12 and 3 beyond.  Results do not depend on the choice.
+int mx4_mode(const moe_weights& W, int T, int k) {
+  const double n = W.num_experts;
+  const double p = std::min(1.0, (double)k / n);
+  const double u = n * (1.0 - std::pow(1.0 - p, (double)T)) + W.num_shared;
+  const double per = (double)T * (k + W.num_shared) / std::max(1.0, u);
+  return per <= 1.5 ? 0 : per <= 4.0 ? 1 : 2;
+}
+
+Mx4Args mx4_args_gate_up(const GateUpArgs& g) {
+  Mx4Args m{};
+  m.w = g.w13;
+  m.ws = reinterpret_cast<const uint8_t*>(g.w13s);
+  m.act = reinterpret_cast<const uint8_t*>(g.x);
+  m.ids = g.ids;
+  m.wts = nullptr;
+  m.out = g.h;
+  m.T = g.T, m.k = g.k, m.slots = g.slots, m.E = g.E, m.n_words = g.n_words;
+  m.n_entries = g.n_entries;
+  m.K = g.H, m.N = g.I, m.row_bytes = g.row_bytes, m.n_groups = g.I / 16;
+  m.slots_magic = g.slots_magic;
+  return m;
+}
+
+Mx4Args mx4_args_down(const DownArgs& d) {
+  Mx4Args m{};
+  m.w = d.w2;
+  m.ws = reinterpret_cast<const uint8_t*>(d.w2s);
+  m.act = reinterpret_cast<const uint8_t*>(d.h);
+  m.ids = d.ids;
+  m.wts = d.wts;
+  m.out = d.y;   // the slot buffer
+  m.T = d.T, m.k = d.k, m.slots = d.slots, m.E = d.E, m.n_words = d.n_words;
+  m.n_entries = d.n_entries;
+  m.K = d.I, m.N = d.H, m.row_bytes = d.row_bytes, m.n_groups = d.H / 32;
+  m.slots_magic = d.slots_magic;
+  return m;
+}
+
+template <bool DOWN, bool HBF16>
+hipError_t launch_mx4(const Mx4Args& a, int mode, hipStream_t s) {
+  // one persistent workgroup per CU (the stage ring takes most of the LDS)
+  const dim3 g(device_num_cus()), b(kBlock);
+  if (mode == 0) hipLaunchKernelGGL((mx4_mfma_kernel<2, 6, DOWN, HBF16>), g, b, 0, s, a);
+  else if (mode == 1) hipLaunchKernelGGL((mx4_mfma_kernel<8, 4, DOWN, HBF16>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((mx4_mfma_kernel<12, 3, DOWN, HBF16>), g, b, 0, s, a);
+  return hipGetLastError();
 }
 
 // Token-major: y[t][d] = sum over slots j (in order) of w_tj * dot(Wd[e_tj][d], h[t][j]).
@@ -1261,11 +1211,10 @@ hipError_t launch_gate_up_decode(const moe_weights& W, const void* x, int x_dtyp
       return hbf ? gate_up_nr<W_MXFP8, false, true>(a, nr, pre, mch, guard, blocks, s)
                  : gate_up_nr<W_MXFP8, false, false>(a, nr, pre, mch, guard, blocks, s);
     case W_MXFP4:
-      if (!xf32 && gate_up_mx4_mfma_fits(W)) {
-        // one persistent workgroup per CU (the stage ring takes most of the LDS)
-        if (hbf) hipLaunchKernelGGL(gate_up_mx4_mfma_kernel<true>, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
-        else hipLaunchKernelGGL(gate_up_mx4_mfma_kernel<false>, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
-        return hipGetLastError();
+      if (!xf32 && mx4_mfma_fits(W)) {
+        const Mx4Args m = mx4_args_gate_up(a);
+        return hbf ? launch_mx4<false, true>(m, mx4_mode(W, T, k), s)
+                   : launch_mx4<false, false>(m, mx4_mode(W, T, k), s);
       }
       return hbf ? gate_up_nr<W_MXFP4, false, true>(a, nr, pre, mch, guard, blocks, s)
                  : gate_up_nr<W_MXFP4, false, false>(a, nr, pre, mch, guard, blocks, s);
@@ -1360,7 +1309,7 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
 int down_variant_for(const moe_weights& W, int T, int k) {
   const long long entries = (long long)T * (k + W.num_shared);
   if (entries > kDecodeMaxEntries) return kDownTokenMajor;
-  if (down_mx4_mfma_fits(W)) return kDownExpertMajor;
+  if (mx4_mfma_fits(W)) return kDownExpertMajor;
   return T > 16 ? kDownExpertMajor : kDownTokenMajor;
 }
 
@@ -1385,10 +1334,8 @@ hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,
                 : down_shape<W_MXFP8, false>(a, p.lpr, em, ybf, p.blocks, s);
       break;
     case W_MXFP4:
-      if (hbf && em == kDownExpertMajor && down_mx4_mfma_fits(W)) {
-        // one persistent workgroup per CU (the stage ring takes most of the LDS)
-        hipLaunchKernelGGL(down_mx4_mfma_kernel, dim3(device_num_cus()), dim3(kBlock), 0, s, a);
-        err = hipGetLastError();
+      if (hbf && em == kDownExpertMajor && mx4_mfma_fits(W)) {
+        err = launch_mx4<true, false>(mx4_args_down(a), mx4_mode(W, T, k), s);
       } else {
         err = hbf ? down_shape<W_MXFP4, true>(a, p.lpr, em, ybf, p.blocks, s)
                   : down_shape<W_MXFP4, false>(a, p.lpr, em, ybf, p.blocks, s);
@@ -1416,5 +1363,28 @@ hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype) {
 }
 
 int down_auto_variant(const moe_weights& W, int T, int k) { return down_variant_for(W, T, k); }
+
+bool decode_on_matrix_cores(const moe_weights& W) { return mx4_mfma_fits(W); }
+
+// Expected number of passes (virtual experts) of the matrix-core kernels
+// under uniform routing: each expert's entry count is Binomial(T, k/E), and an
+// expert with c entries takes ceil(c / TC) passes; shared experts take every
+// token.
+double decode_matrix_core_passes(const moe_weights& W, int T, int k) {
+  static const int kTc[3] = {2, 8, 12};
+  const int tc = kTc[mx4_mode(W, T, k)];
+  const double p = std::min(1.0, (double)k / W.num_experts);
+  const double all = (double)((T + tc - 1) / tc);   // passes of an expert every token uses
+  double per = all;
+  if (p < 1.0) {
+    per = 0.0;
+    double pmf = std::pow(1.0 - p, (double)T);         // P(c = 0)
+    for (int c = 1; c <= T; ++c) {
+      pmf *= (double)(T - c + 1) / c * (p / (1.0 - p));
+      per += pmf * ((c + tc - 1) / tc);
+    }
+  }
+  return W.num_experts * per + W.num_shared * all;
+}
 
 }  // namespace moe

@@ -31,6 +31,10 @@ int down_lanes_per_row(int fmt, int inter, int h_dtype);
 hipError_t decode_supported(const moe_weights& W, int T, int k, int h_dtype);
 // the moe_down_variant MOE_DOWN_AUTO runs for T tokens
 int down_auto_variant(const moe_weights& W, int T, int k);
+// MXFP4 decode runs on the matrix cores for these weights; expected passes
+// over the touched experts' rows at T tokens (path-choice model).
+bool decode_on_matrix_cores(const moe_weights& W);
+double decode_matrix_core_passes(const moe_weights& W, int T, int k);
 
 // align_sort.hip
 size_t align_sort_workspace_bytes(int n_entries, int n_experts);

@@ -274,3 +274,42 @@ def test_mx4_matrix_core_passes_and_shared_expert(lib):
     hh = to_f64(h)
     assert np.max(np.abs(hh - h_ref)) <= 2e-4 * scale + 1e-6, np.max(np.abs(hh - h_ref)) / scale
     assert_layer_close(to_f64(y), y_ref)
+
+
+def test_mx4_matrix_core_results_do_not_depend_on_the_launch_shape(lib):
+    """The MXFP4 matrix-core kernels pick 2, 8 or 12 columns per pass (and the
+    ring depth) from the batch size; a token's h and y are the same bits
+    alone (2 columns) and inside batches of 4 (8 columns), 32 and 256 (12)."""
+    cfg = SMALL["mxfp4"]
+    Wd = device_weights(cfg)
+    t_max = lib.load().moe_decode_max_entries() // cfg.top_k
+    x, ids, w = inputs(cfg, t_max)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    ref = {}
+    for t in (4, 32, t_max):
+        h = lib.gate_up(Wd, xd[:t].contiguous(), idd[:t].contiguous(), h_dtype="bf16")
+        y = lib.down(Wd, h, idd[:t].contiguous(), wd[:t].contiguous())
+        torch.cuda.synchronize()
+        ref[t] = (h[:3].clone(), y[:3].clone())
+    for j in range(3):
+        h1 = lib.gate_up(Wd, xd[j:j + 1].contiguous(), idd[j:j + 1].contiguous(), h_dtype="bf16")
+        y1 = lib.down(Wd, h1, idd[j:j + 1].contiguous(), wd[j:j + 1].contiguous())
+        torch.cuda.synchronize()
+        for t, (h, y) in ref.items():
+            assert torch.equal(h1[0], h[j]) and torch.equal(y1[0], y[j]), (j, t)
+
+
+def test_mx4_matrix_core_expert_count_not_a_multiple_of_64(lib):
+    """72 experts: the work map walks the expert ids 64 at a time."""
+    cfg = W.MXFP4_SWEEP.replace(hidden=512, inter=256, num_experts=72, tag=25)
+    x, ids, w = inputs(cfg, 9)
+    Wd = device_weights(cfg)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd)
+    y = lib.down(Wd, h, idd, wd)
+    torch.cuda.synchronize()
+    h_ref, y_ref = _oracle(cfg, x, ids, w)
+    scale = np.sqrt(np.mean(h_ref ** 2))
+    assert np.max(np.abs(to_f64(h) - h_ref)) <= 2e-4 * scale + 1e-6
+    assert_layer_close(to_f64(y), y_ref)
