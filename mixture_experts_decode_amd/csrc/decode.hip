@@ -516,6 +516,77 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
   }
 }
 
+// Expert-major down with the item's E4M3 rows converted to BF16 once instead
+// of once per routed entry.  The conversion is exact and unscaled, and each
+// chunk's partial sum is still a fresh dot2 chain over the same pairs in the
+// same order, multiplied into the accumulator by the chunk's scale, then the
+// same lane reduction: y keeps the bits of the other two down kernels.  Per
+// entry only the dot products remain.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float acc) {
+  if constexpr (LPR == 32) return half32_sum(acc);
+  else if constexpr (LPR == 16) return row16_sum(acc);
+  else if constexpr (LPR == 8) return group8_sum(acc);
+  else return group4_sum(acc);
+}
+
+template <int FMT, int LPR, int CPL, int RPL>
+MOE_STREAM_KERNEL(RPL * CPL >= 8 ? 3 : 4) void down_expert_pre_kernel(const DownArgs a) {
+  static_assert(FMT == W_MXFP8 || FMT == W_FP8B128, "E4M3 rows");
+  __shared__ int s_ids[kDecodeMaxEntries];
+  __shared__ uint32_t s_mask[kMaskWords];
+  constexpr int ND = kWave / LPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = lane / LPR, gl = lane % LPR;
+  const int U = stage_routing(a.ids, a.k, a.slots, a.E, a.n_words, a.n_entries, s_ids, s_mask);
+  const int n_items = U * a.n_dgroups;
+  const int n_waves = gridDim.x * kWavesPerBlock;
+  float* out = reinterpret_cast<float*>(a.y);
+  for (int it = blockIdx.x * kWavesPerBlock + wave_in_block(); it < n_items; it += n_waves) {
+    const int e = select_rank(s_mask, a.n_words, it / a.n_dgroups);
+    const int d0 = (it % a.n_dgroups) * ND * RPL + grp;
+    DownRow<FMT, CPL> raw[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      load_down_row<FMT, LPR, CPL>(raw[r], a, e, min(d0 + r * ND, a.H - 1), gl, true);
+    // wb[r][i][2d], [2d + 1]: the two BF16 pairs of byte pairs 0-1 and 2-3 of dword d
+    uint32_t wb[RPL][CPL][8];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wb[r][i][2 * d] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(raw[r].w[i][d]));
+          wb[r][i][2 * d + 1] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(raw[r].w[i][d]));
+        }
+    PairIter pi;
+    pairs_begin(pi, s_ids, a.n_entries, e);
+    for (int pe = pairs_next(pi, s_ids, a.n_entries, e); pe >= 0;
+         pe = pairs_next(pi, s_ids, a.n_entries, e)) {
+      XChunk<FMT, false> hc[CPL];
+      load_h_chunks<FMT, LPR, CPL, true>(hc, a, pe, gl);
+      const float w = slot_weight(a, pe);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          float part = 0.f;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            part = dot2_bf16(as_bf16x2(wb[r][i][2 * d]), as_bf16x2(hc[i].v[2 * d]), part);
+            part = dot2_bf16(as_bf16x2(wb[r][i][2 * d + 1]), as_bf16x2(hc[i].v[2 * d + 1]), part);
+          }
+          acc = fmaf(part, raw[r].s[i], acc);
+        }
+        const float dot = lane_group_sum<LPR>(acc);
+        if (gl == 0 && d0 + r * ND < a.H) out[(size_t)pe * a.H + d0 + r * ND] = __fmul_rn(dot, w);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gate_up and down on the matrix cores for E2M1 rows and BF16 activations
 // ---------------------------------------------------------------------------
@@ -1065,7 +1136,20 @@ hipError_t down_launch(const DownArgs& a, int variant, int ybf16, int blocks, hi
   dim3 g(blocks), b(kBlock);
   const bool expert_major = variant == kDownExpertMajor;
   // rows per lane group as the register rule allows (4 up to 3 chunks per
-  // lane, 2 up to 4); nothing wider is compiled
+  // lane, 2 up to 4); nothing wider is compiled.  E4M3 rows with BF16 h take
+  // the kernel that converts each item's rows once.
+  if constexpr ((FMT == W_MXFP8 || FMT == W_FP8B128) && HBF16 && CPL <= 4) {
+    if (expert_major && (a.rpl == 4 || a.rpl == 2)) {
+      if constexpr (CPL <= 3) {
+        if (a.rpl == 4) {
+          hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 4>), g, b, 0, s, a);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 2>), g, b, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (CPL <= 3) {
     if (expert_major && a.rpl == 4) {
       hipLaunchKernelGGL((down_expert_kernel<FMT, LPR, CPL, 4, HBF16>), g, b, 0, s, a);
