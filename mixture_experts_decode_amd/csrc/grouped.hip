@@ -117,19 +117,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ s
     const size_t t = i / h4;
     const size_t c = i - t * h4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < slots; ++j) {
-      float4 v;
-      if constexpr (SBF16) {
-        const uint2 q =
-            reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(so) + (t * slots + j) * H)[c];
-        v = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-      } else {
-        v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(so) + (t * slots + j) * H)[c];
+    // up to eight slots' loads are issued before their adds (in slot order)
+    for (int j0 = 0; j0 < slots; j0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < slots) {
+          if constexpr (SBF16) {
+            const uint2 q = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(so) +
+                                                           (t * slots + j) * H)[c];
+            v[u] = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+          } else {
+            v[u] = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(so) +
+                                                   (t * slots + j) * H)[c];
+          }
+        }
       }
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < slots) {
+          acc.x += v[u].x;
+          acc.y += v[u].y;
+          acc.z += v[u].z;
+          acc.w += v[u].w;
+        }
+      }
     }
     if constexpr (YBF16) {
       uint2 o;

@@ -193,7 +193,11 @@ def test_duplicate_ids_within_a_token(lib):
 
 FULL = [("qwen3_decode_mxfp8", 32, None), ("qwen3_decode_mxfp8", 1, None),
         ("deepseek_v3_fp8_blk128", 16, None), ("mxfp4_sweep", 64, None),
-        ("mxfp4_sweep", 32, "zipf")]
+        ("mxfp4_sweep", 32, "zipf"),
+        # the MXFP4 matrix-core kernels' other launch shapes at full size: two
+        # columns per pass (B = 1) and twelve with two passes per expert
+        # (B = 256, Zipf: hot experts split over many wavefronts)
+        ("mxfp4_sweep", 1, None), ("mxfp4_sweep", 256, "zipf")]
 
 
 @pytest.mark.parametrize("name,t,kind", FULL)
