@@ -231,9 +231,12 @@ def main():
         h_el = 4 if cfg.fmt == "f32" else 2
         gate_up_bytes = u * (ebytes - ebytes_dn) + b * cfg.hidden * act_bytes + ids.nbytes \
             + b * slots * cfg.inter * h_el
+        # down product: the touched experts' W_down, h, routing, and y
+        down_bytes = u * ebytes_dn + b * slots * cfg.inter * h_el + ids.nbytes + wts.nbytes \
+            + b * cfg.hidden * 4
         return dict(x=to_dev_x(torch, dev, cfg, x), ids=torch.from_numpy(ids).to(dev),
                     wts=torch.from_numpy(wts).to(dev), bytes=u * ebytes + io,
-                    gate_up_bytes=gate_up_bytes, U=u, np=(x, ids, wts))
+                    gate_up_bytes=gate_up_bytes, down_bytes=down_bytes, U=u, np=(x, ids, wts))
 
     h_dtype = "f32" if cfg.fmt == "f32" else "bf16"   # as moe_layer's decode path
 
@@ -352,17 +355,29 @@ def main():
             del gg
             res["gate_up_graph_us"] = s0.elapsed_time(s1) * 1e3 / steps
             res["gate_up_graph_GBps"] = gub / (s0.elapsed_time(s1) * 1e-3) / 1e9
+            # the down product alone in both launch shapes, timed the same
+            # way; GB/s counts the down product's algorithmic bytes (the
+            # expert-major shape also writes and re-reads its slot outputs)
+            dnb = sum(ins[i % n_layers]["down_bytes"] for i in range(steps)) / steps
             res["down_variants_us"] = {}
+            res["down_variants_frac"] = {}
             for var in ("token", "expert"):
-                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-                for i in range(steps):
-                    L, d = layers[i % n_layers], ins[i % n_layers]
-                    ev[i][0].record(stream)
-                    moe.down(L, h, d["ids"], d["wts"], y=y, variant=var, workspace=dws)
-                    ev[i][1].record(stream)
+                gd = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gd):
+                    for i in range(steps):
+                        L, d = layers[i % n_layers], ins[i % n_layers]
+                        moe.down(L, h, d["ids"], d["wts"], y=y, variant=var, workspace=dws)
                 torch.cuda.synchronize()
-                res["down_variants_us"][var] = round(
-                    float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3, 2)
+                gd.replay()
+                s0.record(stream)
+                gd.replay()
+                s1.record(stream)
+                torch.cuda.synchronize()
+                del gd
+                us = s0.elapsed_time(s1) * 1e3 / steps
+                res["down_variants_us"][var] = round(us, 2)
+                res["down_variants_frac"][var] = round(dnb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            res["down_bytes_per_launch"] = dnb
         log(f"{cfg.name} B={b} {chosen}: {res['us_per_layer']:.1f} us, {res['TBps']:.3f} TB/s, "
             f"parity {par}")
         return res
@@ -376,7 +391,7 @@ def main():
             r = run_steps(b, 50, 5, args.path, n_check=None)
             sweep.append(rounded(r, ("B", "path", "us_per_layer", "eager_us_per_layer", "replays_us",
                                      "TBps", "frac_of_copy_peak", "U_mean", "gate_up_us",
-                                     "down_us", "down_variants_us", "parity")))
+                                     "down_us", "down_variants_us", "down_variants_frac", "parity")))
 
     roofline = None
     if main_res["path"] == "decode":
@@ -473,6 +488,9 @@ def main():
         "frac_of_hbm_peak": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(main_res[k], 2) for k in ("gate_up_us", "down_us") if k in main_res},
         "down_variants_us": main_res.get("down_variants_us"),
+        "down_variants_frac_of_hbm_peak": main_res.get("down_variants_frac"),
+        "down_bytes_per_launch": round(main_res["down_bytes_per_launch"])
+        if "down_bytes_per_launch" in main_res else None,
         "sweep": sweep,
         "layers": layers_sweep,
         "roofline": roofline,

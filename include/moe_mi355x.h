@@ -132,7 +132,8 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
 
 /* Launch shapes of moe_down (identical bits, with the MXFP4 exception below). */
 typedef enum {
-  MOE_DOWN_AUTO = 0,          /* token-major up to 16 tokens, else expert-major;
+  MOE_DOWN_AUTO = 0,          /* token-major for small batches, expert-major from
+                                 a number of routed entries on (see moe_down);
                                  expert-major at every T for MXFP4 rows that fit
                                  the matrix-core kernel (see below)             */
   MOE_DOWN_TOKEN_MAJOR = 1,   /* a wavefront owns (token, rows); no buffer        */
@@ -156,8 +157,11 @@ typedef enum {
  *                          rows once for all tokens routed to the expert and
  *                          stores w * dot per (token, slot) in the workspace;
  *                          a combine kernel adds them in slot order.
- *   MOE_DOWN_AUTO          token-major up to 16 tokens, expert-major beyond
- *                          (measured faster on each side of that line).
+ *   MOE_DOWN_AUTO          token-major below a number of routed entries
+ *                          (T * slots), expert-major from it on, measured
+ *                          faster on each side of that line: 112 entries
+ *                          when a W_down row spans fewer than 32 lanes (I up
+ *                          to about 1024 with BF16 h), 18 from 32 lanes on.
  * The exception: MXFP4 weights with BF16 h, I a multiple of 256 and H of 32.
  * Their expert-major shape runs on the matrix cores (the expert's routed
  * entries as the columns of v_mfma_f32_16x16x32_bf16): the same exact

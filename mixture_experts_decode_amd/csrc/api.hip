@@ -172,8 +172,8 @@ size_t decode_h_bytes(const moe_weights* W, int32_t T, int32_t k) {
   return align_up((size_t)T * (k + W->num_shared) * W->inter * el);
 }
 
-// The decode path's workspace: h, then (for the expert-major down variant,
-// used from 17 tokens up) the FP32 slot outputs.
+// The decode path's workspace: h, then (when AUTO runs the down product
+// expert-major) the FP32 slot outputs.
 size_t decode_slot_bytes(const moe_weights* W, int32_t T, int32_t k) {
   if (moe::down_auto_variant(*W, T, k) != MOE_DOWN_EXPERT_MAJOR) return 0;
   return align_up((size_t)T * (k + W->num_shared) * W->hidden * 4);

@@ -24,8 +24,9 @@
 //      - expert-major: a wavefront owns (expert, output rows), reads those
 //        rows once and writes w * dot for every (token, slot) routed to the
 //        expert; a small combine kernel then sums the slots in slot order.
-//        Used from 17 tokens up, where it was measured faster: rows shared by
-//        several tokens are read once instead of once per (token, slot).
+//        Used from a number of routed entries up (see down_variant_for),
+//        where it was measured faster: rows shared by several tokens are
+//        read once instead of once per (token, slot).
 //  * MXFP4 gate_up (E2M1 rows, BF16 activations) runs on the matrix cores
 //    instead: a wavefront owns (expert, 16 neurons) with the expert's routed
 //    entries as MFMA columns, and streams 128-byte row slices through an LDS
@@ -1382,19 +1383,29 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
 
 }  // namespace
 
-// AUTO: token-major up to 16 tokens, expert-major beyond (and within the
-// entries it stages).  Measured on the Qwen3-style layer (down alone,
-// MI355X): B = 4, 8, 16: 13.1 / 22.6 / 36.7 us token-major against 17.4 /
-// 27.0 / 38.1 expert-major; B = 32: 59.4 against 53.8 (the expert-major rows
-// are read once for all the tokens routed to them; the token-major ones once
-// per (token, slot), from L2 after the first).  MXFP4 rows that fit the
-// matrix-core kernel take expert-major at every batch size, so that a token's
-// y does not change with the batch size there either.
+// AUTO: token-major for small batches, expert-major from a number of routed
+// entries on (within the entries it stages).  The token-major kernel reads a
+// routed expert's rows once per (token, slot), from L2 after the first, and a
+// wavefront holds 64/LPR rows of one entry; the expert-major kernel reads them
+// once per call and holds 64/LPR x 2-4 rows, at the price of the slot buffer
+// and the combine kernel.  The crossover follows the lanes per row (BF16 h;
+// FP32 h with FP32 weights).  Measured, down alone, graph-replayed, MI355X,
+// token-major / expert-major:
+//  * 16 lanes per row (Qwen3-style layer, I = 768): 13 tokens 29.1 / 29.4 us,
+//    14 tokens 30.8 / 30.3 us, 16 tokens 35.0 / 32.2, 32 tokens 56.6 / 44.1:
+//    expert-major from 112 entries;
+//  * 32 lanes per row (MXFP8, I = 1536: 2 tokens 22.3 / 24.4 us, 4 tokens
+//    37.5 / 34.0; DeepSeek-V3-shaped, 9 slots: 1 token 29.2 / 30.2, 2 tokens
+//    52.4 / 48.5): expert-major from 18 entries.
+// The two give identical bits, so the switch does not change any result.
+// MXFP4 rows that fit the matrix-core kernel take expert-major at every batch
+// size, so that a token's y does not change with the batch size there either.
 int down_variant_for(const moe_weights& W, int T, int k) {
   const long long entries = (long long)T * (k + W.num_shared);
   if (entries > kDecodeMaxEntries) return kDownTokenMajor;
   if (mx4_mfma_fits(W)) return kDownExpertMajor;
-  return T > 16 ? kDownExpertMajor : kDownTokenMajor;
+  const int lpr = lanes_per_row_for(W.format, W.inter, W.format == W_F32 ? MOE_DT_F32 : MOE_DT_BF16);
+  return entries >= (lpr >= 32 ? 18 : 112) ? kDownExpertMajor : kDownTokenMajor;
 }
 
 hipError_t launch_down_decode(const moe_weights& W, const void* h, int h_dtype,

@@ -95,7 +95,7 @@ def test_host_argument_errors(lib):
                         None) == moe.ERR_INVALID_ARG
     assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, 2, dummy, 64,
                         None) == moe.ERR_WORKSPACE_TOO_SMALL
-    # AUTO runs expert-major from 17 tokens up, which needs the workspace
+    # AUTO runs expert-major from 112 entries up here, which needs the workspace
     assert lib.moe_down(ctypes.byref(w), dummy, 0, dummy, dummy, 32, 8, dummy, 0, 0, None, 0,
                         None) == moe.ERR_INVALID_ARG
     assert lib.moe_down_workspace_bytes(ctypes.byref(w), 4, 8) == 4 * 8 * 2048 * 4
@@ -161,9 +161,15 @@ def test_path_choice_host_logic(lib):
     w32 = _weights(__import__("mixture_experts_decode_amd"), format=0)
     assert lib.moe_choose_path(ctypes.byref(w32), 16384, 8) == DEC
     # workspace sizes: decode = h (T*slots*I, BF16), plus the FP32 slot
-    # outputs of the expert-major down from 17 tokens up
+    # outputs of the expert-major down, which AUTO runs from 112 entries up
+    # when a W_down row spans 16 lanes (I = 768) and from 18 entries up at 32
+    # lanes (the measured crossovers)
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, DEC, 64) == 32 * 8 * (768 * 2 + 2048 * 4)
-    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 16, 8, DEC, 64) == 16 * 8 * 768 * 2
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 14, 8, DEC, 64) == 14 * 8 * (768 * 2 + 2048 * 4)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 13, 8, DEC, 64) == 13 * 8 * 768 * 2
+    ds = _weights(moe, hidden=7168, inter=2048, num_experts=256, num_shared=1, format=3)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(ds), 1, 8, DEC, 64) == 9 * 2048 * 2
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(ds), 2, 8, DEC, 64) == 18 * (2048 * 2 + 7168 * 4)
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 64) > 0
     assert lib.moe_layer_workspace_bytes(ctypes.byref(w), 32, 8, GRP, 48) == 0
     # block 0: the library picks by expected entries per expert (32 at 2 per
