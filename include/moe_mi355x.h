@@ -33,7 +33,8 @@
  *  - Preconditions NOT checked (they would need a device read): expert ids in
  *    [0, num_experts); finite weights and scales; outputs not aliasing inputs.
  *    Every kernel reads an id outside [0, num_experts) as expert 0, so such an
- *    id never takes an access outside the caller's buffers.
+ *    id never takes an access outside the caller's buffers; moe_check_routing
+ *    finds such ids on the device when a caller wants them checked.
  *  - The library keeps no mutable global state apart from a per-device cache
  *    of the compute-unit count; calls are thread-safe.  Calls may be captured
  *    in a HIP graph: they record kernels only.
@@ -329,6 +330,25 @@ moe_status moe_combine(const uint16_t* slot_out, int32_t T, int32_t slots, int32
  */
 moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int32_t E,
                           int32_t k, int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * moe_check_routing: checks on the device the one precondition the layer's
+ * entry points take on trust: every routed id is the index of one of the E
+ * experts the router chooses among (align-and-sort article, background
+ * section: each token activates k of the E experts), i.e. lies in
+ * [0, num_experts).  Writes
+ *   result[0] = the number of entries of topk_ids outside [0, num_experts)
+ *   result[1] = the first such entry, t*k + j, or -1 if there is none
+ *   topk_ids device [T][k] int32; result device int32[2] (caller-owned).
+ * One kernel of one workgroup; nothing is read back to the host and nothing
+ * needs clearing first, so it can be enqueued (or captured) ahead of the
+ * layer and its result read whenever the caller synchronises.
+ * Sizes: T >= 0, k >= 1, num_experts >= 1; T*k <= 2^31 - 1, else
+ * MOE_ERR_UNSUPPORTED.  Errors: MOE_ERR_INVALID_ARG for bad sizes or a null
+ * pointer (nothing enqueued).  T == 0 writes {0, -1}.
+ */
+moe_status moe_check_routing(const int32_t* topk_ids, int32_t T, int32_t k, int32_t num_experts,
+                             int32_t* result, void* stream);
 
 /* ------------------------------------------------------------------ */
 /* The whole layer.                                                     */

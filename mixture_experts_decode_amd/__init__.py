@@ -60,6 +60,7 @@ _SIGS = {
     "moe_grouped_down": (_I, [_WP, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _I, _I, _I, _P, _I, _P]),
     "moe_topk_route": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "moe_check_routing": (_I, [_P, _I, _I, _I, _P, _P]),
     "moe_choose_path": (_I, [_WP, _I, _I]),
     "moe_layer_workspace_bytes": (_Z, [_WP, _I, _I, _I, _I]),
     "moe_layer": (_I, [_WP, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _Z,
@@ -306,6 +307,21 @@ def topk_route(scores, k, bias=None, ids=None, wts=None, stream=None):
                              _ptr(wts), _stream(stream))
     _check(st, "moe_topk_route")
     return ids, wts
+
+
+@_on_stream
+def check_routing(ids, num_experts, result=None, stream=None):
+    """Device check of topk_ids [T][k] int32: returns (or fills) an int32 [2]
+    device tensor (number of ids outside [0, num_experts), first such entry
+    t*k + j or -1)."""
+    load()
+    t, k = ids.shape
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=ids.device)
+    st = _lib.moe_check_routing(_ptr(ids) if ids.numel() else None, t, k, num_experts,
+                                _ptr(result), _stream(stream))
+    _check(st, "moe_check_routing")
+    return result
 
 
 def choose_path(W, t, k):

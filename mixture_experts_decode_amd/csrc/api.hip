@@ -391,6 +391,15 @@ moe_status moe_topk_route(const float* scores, const float* bias, int32_t T, int
                                          as_stream(stream)));
 }
 
+moe_status moe_check_routing(const int32_t* topk_ids, int32_t T, int32_t k, int32_t num_experts,
+                             int32_t* result, void* stream) {
+  if (T < 0 || k < 1 || num_experts < 1) return MOE_ERR_INVALID_ARG;
+  if (!result || (T > 0 && !topk_ids)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_check_routing(topk_ids, T * k, num_experts, result,
+                                            as_stream(stream)));
+}
+
 int32_t moe_choose_path(const moe_weights* W, int32_t T, int32_t k) {
   if (check_weights(W) != MOE_OK || check_routing(W, T, k) != MOE_OK) return MOE_PATH_DECODE;
   if (!grouped_supported(W) || W->hidden % 128 || W->inter % 128) return MOE_PATH_DECODE;

@@ -55,6 +55,8 @@ hipError_t launch_grouped_down(const moe_weights& W, const uint8_t* hq, const ui
                                int T, int k, uint16_t* slot_out, hipStream_t s);
 hipError_t launch_topk_route(const float* scores, const float* bias, int T, int E, int k,
                              int32_t* ids, float* wts, hipStream_t s);
+// out[0] = ids outside [0, E) among ids[0 .. n), out[1] = the first (-1: none)
+hipError_t launch_check_routing(const int32_t* ids, int n, int E, int32_t* out, hipStream_t s);
 // slot_dtype MOE_DT_F32 (decode path) or MOE_DT_BF16 (grouped path)
 hipError_t launch_combine(const void* slot_out, int slot_dtype, int T, int slots, int H, void* y,
                           int y_dtype, hipStream_t s);

@@ -103,4 +103,55 @@ hipError_t launch_topk_route(const float* scores, const float* bias, int T, int 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Routing check: how many routed ids lie outside [0, E), and the first one.
+// One workgroup walks all T*k ids and writes the two numbers once, so nothing
+// has to be cleared before it (no memset, safe inside a captured graph) and
+// the result does not depend on any scheduling.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kCheckBlock = 1024;
+
+__global__ __launch_bounds__(kCheckBlock) void check_routing_kernel(const int32_t* __restrict__ ids,
+                                                                    int n, int E,
+                                                                    int32_t* __restrict__ out) {
+  __shared__ int s_cnt[kCheckBlock / kWave];
+  __shared__ int s_first[kCheckBlock / kWave];
+  int cnt = 0, first = n;
+  for (long long i = threadIdx.x; i < n; i += kCheckBlock) {
+    if ((unsigned)ids[i] >= (unsigned)E) {
+      ++cnt;
+      first = min(first, (int)i);
+    }
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, kWave);
+    first = min(first, __shfl_xor(first, off, kWave));
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    s_cnt[w] = cnt;
+    s_first[w] = first;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0, f = n;
+    for (int q = 0; q < kCheckBlock / kWave; ++q) {
+      c += s_cnt[q];
+      f = min(f, s_first[q]);
+    }
+    out[0] = c;
+    out[1] = f < n ? f : -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_check_routing(const int32_t* ids, int n, int E, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(check_routing_kernel, dim3(1), dim3(kCheckBlock), 0, s, ids, n, E, out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

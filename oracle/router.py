@@ -36,3 +36,12 @@ def topk_route(scores, k, bias=None):
     sel = np.take_along_axis(s32.astype(np.float64), ids.astype(np.int64), axis=1)
     z = np.exp(sel - sel.max(axis=1, keepdims=True))
     return ids, z / z.sum(axis=1, keepdims=True)
+
+
+def check_routing(ids, num_experts):
+    """(number of routed ids outside [0, num_experts), first such flat entry
+    t*k + j or -1).  The routed ids index k of the E experts a token activates
+    (align-and-sort article, background section), so [0, E) is their range."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    bad = np.flatnonzero((flat < 0) | (flat >= num_experts))
+    return int(bad.size), (int(bad[0]) if bad.size else -1)

@@ -101,6 +101,13 @@ def test_host_argument_errors(lib):
     assert lib.moe_down_workspace_bytes(ctypes.byref(w), 4, 8) == 4 * 8 * 2048 * 4
     # T == 0 is a no-op
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 0, 8, dummy, 0, None) == moe.OK
+    # routing check: sizes and pointers refused before any launch
+    assert lib.moe_check_routing(dummy, -1, 8, 128, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_check_routing(dummy, 4, 0, 128, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_check_routing(dummy, 4, 8, 0, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_check_routing(dummy, 4, 8, 128, None, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_check_routing(None, 4, 8, 128, dummy, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_check_routing(dummy, 1 << 28, 16, 128, dummy, None) == moe.ERR_UNSUPPORTED
     # align-sort: block size, workspace
     assert lib.moe_align_sort(dummy, 4, 8, 128, 0, 0, dummy, dummy, dummy, dummy, dummy, 1 << 20,
                               None) == moe.ERR_INVALID_ARG

@@ -102,3 +102,38 @@ def test_router_feeds_the_layer(lib, path):
     ref = L.moe_layer(L.activations_f64(x, cfg.act), ref_ids.astype(np.int32),
                       ref_w.astype(np.float32), act_quant=mode, **oracle_kw(cfg))
     assert_layer_close(to_f64(y), ref, path)
+
+
+@pytest.mark.parametrize("t,k,e,bad", [(0, 8, 128, []), (1, 8, 128, []), (32, 8, 128, [5, 77, 200]),
+                                       (300, 9, 257, [0, 1, 2699]), (16384, 8, 256, [131071])])
+def test_check_routing_counts_out_of_range_ids(t, k, e, bad):
+    import mixture_experts_decode_amd as moe
+    rng = np.random.default_rng(11)
+    ids = rng.integers(0, e, size=(t, k)).astype(np.int32)
+    flat = ids.reshape(-1)
+    for i, p in enumerate(bad):
+        flat[p] = (-1, e, 2**31 - 1, -2**31)[i % 4]
+    res = moe.check_routing(torch.from_numpy(ids).cuda(), e)
+    torch.cuda.synchronize()
+    assert tuple(int(v) for v in res.cpu().numpy()) == R.check_routing(ids, e)
+
+
+def test_check_routing_in_a_captured_graph():
+    # the check records one kernel and writes its result without a clear, so a
+    # graph replays it correctly after the ids change in place
+    import mixture_experts_decode_amd as moe
+    ids = torch.zeros((64, 8), dtype=torch.int32, device="cuda")
+    res = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    moe.check_routing(ids, 128, result=res)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.check_routing(ids, 128, result=res)
+    for step, planted in enumerate(([], [40], [3, 511], [])):
+        ids.zero_()
+        for p in planted:
+            ids.view(-1)[p] = 128
+        g.replay()
+        torch.cuda.synchronize()
+        want = (len(planted), min(planted) if planted else -1)
+        assert tuple(int(v) for v in res.cpu().numpy()) == want, step

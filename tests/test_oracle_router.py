@@ -103,3 +103,20 @@ def test_weights_closed_forms(shift):
     idsa, wa = R.topk_route(s, 32)
     full = softmax(s.astype(np.float64), axis=1)
     assert np.allclose(wa, np.take_along_axis(full, idsa.astype(np.int64), axis=1), rtol=1e-13)
+
+
+def test_check_routing_hand_worked_and_brute_force():
+    # hand-worked: E = 4; entries 2 (id 4) and 3 (id -1) are out of range
+    assert R.check_routing(np.array([[0, 3], [4, -1]], dtype=np.int32), 4) == (2, 2)
+    assert R.check_routing(np.zeros((0, 8), dtype=np.int32), 4) == (0, -1)
+    # brute force over small random cases: a plain loop over the entries
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        t, k, e = int(rng.integers(0, 6)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        ids = rng.integers(-3, e + 3, size=(t, k)).astype(np.int32)
+        cnt, first = 0, -1
+        for i, v in enumerate(ids.reshape(-1).tolist()):
+            if not 0 <= v < e:
+                cnt += 1
+                first = i if first < 0 else first
+        assert R.check_routing(ids, e) == (cnt, first)
