@@ -408,6 +408,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and not args.headline_only:
         cpu = cpu_baseline(cfg, B, oracle)
+        cpu["align_sort"] = cpu_align_sort_baseline()
     del layers, w0
     torch.cuda.empty_cache()
 
@@ -823,6 +824,27 @@ def cpu_baseline(cfg, B, oracle, budget_s=12.0, max_calls=8):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{calls} whole layer calls of {cfg.name} at B={B} (successive routing "
                       f"draws, {min(touched)}-{max(touched)} touched experts), float64"}
+
+
+def cpu_align_sort_baseline(budget_s=3.0, max_calls=5):
+    """The align-sort oracle (plain Python, one thread) timed on the prefill
+    shape the grouped report sorts on the GPU: 16384 tokens x top-8 over 256
+    experts, Zipf routing, 128-entry blocks (successive routing draws)."""
+    import workloads as W
+    from oracle import align_sort as A
+    c, t, bs = W.PREFILL_ZIPF_MXFP8, 16384, 128
+    spent, calls = 0.0, 0
+    while calls < max_calls and (calls == 0 or spent < budget_s):
+        ids, _ = W.routing(c, t, kind="zipf", variant=calls)
+        t0 = time.perf_counter()
+        A.align_sort(ids.reshape(-1), c.num_experts, bs)
+        spent += time.perf_counter() - t0
+        calls += 1
+    n = t * c.top_k
+    return {"value": round(n * calls / spent / 1e6, 3), "unit": "M entries/s", "cores": 1,
+            "kind": "oracle", "us_per_call": round(spent / calls * 1e6, 1),
+            "sample": f"{calls} calls of oracle.align_sort on {t} tokens x top-{c.top_k} over "
+                      f"{c.num_experts} experts (Zipf routing), {bs}-entry blocks"}
 
 
 if __name__ == "__main__":
