@@ -275,6 +275,7 @@ template <int P>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (P == 8) return (r & 7) ^ ((r >> 3) & 1);
   else if constexpr (P == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  else if constexpr (P == 16) return r & 15;
   else return ((r >> 2) ^ (r >> 3)) & 1;
 }
 
@@ -307,9 +308,14 @@ struct GemmShape {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr bool AS_COOP = WM == 1 && BM == 128 && WAVES == 4;
   static constexpr int SA = WROWS < 64 ? 64 : WROWS;
-  static constexpr int AS_BYTES = AS_COOP ? TERMS * 4 * 64 * 4 : WAVES * TERMS * SA * 4;
+  // scale dwords (four 32-K blocks each) per row and stage; a 64-K stage
+  // reads half a dword
+  static constexpr int SD = KSTEPS >= 2 ? KSTEPS / 2 : 1;
+  static constexpr int AS1 = AS_COOP ? TERMS * 4 * 64 * 4 : WAVES * TERMS * SA * 4;
+  static constexpr int AS_BYTES = SD * AS1;
   static constexpr int SB = T128 ? 64 : (WCOLS < 64 ? 64 : WCOLS);   // per wavefront
-  static constexpr int BS_BYTES = WAVES * SB * 4;
+  static constexpr int BS1 = WAVES * SB * 4;
+  static constexpr int BS_BYTES = SD * BS1;
   static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
   static constexpr int NS_FIT = kLdsBytes / STAGE;
   static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;
@@ -317,8 +323,8 @@ struct GemmShape {
   static constexpr int B_INSTR = B_BYTES / 1024 / WAVES;
   static constexpr int SA_INSTR = AS_COOP ? TERMS : TERMS * (SA / 64);
   static constexpr int SB_INSTR = SB / 64;
-  static constexpr int L = A_INSTR + B_INSTR + SA_INSTR + SB_INSTR;   // DMA ops per stage
-  static_assert(KSTEPS == 1 || KSTEPS == 2, "stage depth");
+  static constexpr int L = A_INSTR + B_INSTR + SD * (SA_INSTR + SB_INSTR);   // DMA ops per stage
+  static_assert(KSTEPS == 1 || KSTEPS == 2 || (KSTEPS == 4 && FP4), "stage depth");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight wavefronts");
   static_assert(WROWS % 32 == 0 && WCOLS % 32 == 0, "whole fragments");
   static_assert(!GATEUP || NF % 2 == 0, "gate and up fragments pair up");
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
     }
   };
 
-  // stage s reads the scale dword holding K blocks [4 * (s*KSTEPS/2), +4)
+  // stage s reads the SD scale dwords from the one holding K block 2 * s * KSTEPS
   auto issue = [&](int s, int buf) {
     uint8_t* base = lds + buf * S::STAGE;
     const int ks = s * S::KSTAGE;                   // first K element of the stage
@@ -487,14 +493,19 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
     const int sdw = (ks >> 7) * 4;                  // byte offset of the scale dword
     uint8_t* as_lds = base + S::A_BYTES + S::B_BYTES;
 #pragma unroll
-    for (int q = 0; q < S::SA_INSTR; ++q) {
-      const int tm = S::AS_COOP ? q : q / (S::SA / 64);
-      dma4((tm ? sa_base1 : sa_base0) + sdw + sa_src[q], as_lds + sa_dst[q]);
-    }
+    for (int d = 0; d < S::SD; ++d)
+#pragma unroll
+      for (int q = 0; q < S::SA_INSTR; ++q) {
+        const int tm = S::AS_COOP ? q : q / (S::SA / 64);
+        dma4((tm ? sa_base1 : sa_base0) + sdw + 4 * d + sa_src[q], as_lds + d * S::AS1 + sa_dst[q]);
+      }
     uint8_t* bs_lds = as_lds + S::AS_BYTES + w * S::SB * 4;
 #pragma unroll
-    for (int u = 0; u < S::SB_INSTR; ++u)
-      dma4(sb_base + (S::T128 ? (ks >> 7) * 4 : sdw) + sb_src[u], bs_lds + 64 * u * 4);
+    for (int d = 0; d < S::SD; ++d)
+#pragma unroll
+      for (int u = 0; u < S::SB_INSTR; ++u)
+        dma4(sb_base + (S::T128 ? (ks >> 7) * 4 : sdw + 4 * d) + sb_src[u],
+             bs_lds + d * S::BS1 + 64 * u * 4);
   };
 
   // acc[m][f]: 32 weight rows of fragment f (MFMA rows) x 32 sorted rows of
@@ -518,30 +529,34 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
     const uint8_t* bt = base + S::A_BYTES;
     const uint32_t* as_lds = reinterpret_cast<const uint32_t*>(base + S::A_BYTES + S::B_BYTES);
     const uint32_t* bs_lds = as_lds + S::AS_BYTES / 4 + w * S::SB;
-    uint32_t sa[TERMS][MF];
+    uint32_t sa[S::SD][TERMS][MF];
 #pragma unroll
-    for (int tm = 0; tm < TERMS; ++tm)
+    for (int d = 0; d < S::SD; ++d)
 #pragma unroll
-      for (int m = 0; m < MF; ++m) {
-        if constexpr (S::AS_COOP) sa[tm][m] = as_lds[tm * 256 + m * 64 + r32];
-        else sa[tm][m] = as_lds[(w * TERMS + tm) * S::SA + 32 * m + r32];
-      }
-    uint32_t sb[NF];
+      for (int tm = 0; tm < TERMS; ++tm)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+          if constexpr (S::AS_COOP) sa[d][tm][m] = as_lds[d * S::AS1 / 4 + tm * 256 + m * 64 + r32];
+          else sa[d][tm][m] = as_lds[d * S::AS1 / 4 + (w * TERMS + tm) * S::SA + 32 * m + r32];
+        }
+    uint32_t sb[S::SD][NF];
     float tsc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (S::T128) {
         tsc[f] = __uint_as_float(bs_lds[f]);
-        sb[f] = 0x7f7f7f7fu;
+        sb[0][f] = 0x7f7f7f7fu;
       } else {
-        sb[f] = bs_lds[32 * f + r32];
+#pragma unroll
+        for (int d = 0; d < S::SD; ++d) sb[d][f] = bs_lds[d * S::BS1 / 4 + 32 * f + r32];
       }
     }
     // byte of the scale dword for K step st of this stage, K block h
     const int sbyte0 = KSTEPS == 2 ? 0 : 2 * (s & 1);
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      const int sh = 8 * (sbyte0 + 2 * st + h);
+      const int ds = KSTEPS >= 2 ? st >> 1 : 0;        // scale dword of this K step
+      const int sh = KSTEPS >= 2 ? 8 * (2 * (st & 1) + h) : 8 * (sbyte0 + h);
       i32x8 bf[NF];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -565,10 +580,10 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const GemmAr
           const u32x4 q1 = *reinterpret_cast<const u32x4*>(ar + a_off[st][1]);
           const i32x8 af = {(int)q0[0], (int)q0[1], (int)q0[2], (int)q0[3],
                             (int)q1[0], (int)q1[1], (int)q1[2], (int)q1[3]};
-          const int sca = (int)((sa[tm][m] >> sh) & 0xffu);
+          const int sca = (int)((sa[ds][tm][m] >> sh) & 0xffu);
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
-            const int scb = (int)((sb[f] >> sh) & 0xffu);
+            const int scb = (int)((sb[ds][f] >> sh) & 0xffu);
             // weights as the first (row) operand, activations as the second
             if constexpr (S::T128) {
               part[m][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -752,6 +767,16 @@ hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
     if constexpr (!GATEUP && BFMT != W_FP8B128) {
       MOE_GG(32, 512, 1, 8, 2);
       return hipGetLastError();
+    }
+    // E2M1 weights: 256-K stages, so each weight row's slice of a stage is a
+    // whole 128-byte line (128-K stages fetch half lines); measured on the
+    // MXFP4 layer, outputs bit for bit the same: B = 128 314 -> 300 us,
+    // B = 256 332 -> 311 us.  The down product gained nothing this way.
+    if constexpr (BFMT == W_MXFP4) {
+      if (a.K % 256 == 0) {
+        MOE_GG(32, 256, 1, 4, 4);
+        return hipGetLastError();
+      }
     }
     MOE_GG(32, 256, 1, 4, 2);
   } else if (bs == 64) {
