@@ -107,11 +107,15 @@ double expert_bytes(const moe_weights* W) {
 //           the smaller of the two showing through, plus 4 us;
 //           For E2M1 weights both decode kernels run on the matrix cores
 //           and stream an expert's rows once per pass of up to 2, 8 or 12
-//           entries: the expected passes times an expert's bytes at
-//           4.4 TB/s, plus 0.03 us per entry and 14 us.
-//  grouped: the same bytes at 5.2 TB/s (4.0 TB/s for E2M1 weights, whose
-//           stage rows are half cache lines) with the matrix work hidden,
-//           plus 25 us for sort, quantisation, combine and launches.
+//           entries: the touched experts' bytes at 4.86 TB/s, the bytes of
+//           the further passes at 5.99 TB/s, 0.081 us per entry and 12.1 us;
+//  grouped: the same bytes at 5.2 TB/s with the matrix work hidden, plus
+//           25 us for sort, quantisation, combine and launches; for E2M1
+//           weights 5.11 TB/s, 0.0057 us per entry and 42.8 us.
+// (The E2M1 constants are a least-squares fit to both paths measured at
+// B = 1, 2, 8, 24, 32, 40, 48, 56, 64, 96, 128, 256; the fit switches at
+// 33 tokens, the measurements between 40 and 48 under uniform routing and
+// below 24 under Zipf routing.)
 // The touched experts are their expectation under uniform routing; skewed
 // routing touches fewer, which favours the grouped path a little earlier
 // than this predicts.
@@ -123,14 +127,15 @@ int32_t model_path(const moe_weights* W, int32_t T, int32_t k) {
   const double entries = (double)T * (k + W->num_shared);
   double t_dec;
   if (moe::decode_on_matrix_cores(*W)) {
-    t_dec = moe::decode_matrix_core_passes(*W, T, k) * expert_bytes(W) / 4.4e6 + 0.03 * entries +
-            14.0;
+    const double extra = std::max(0.0, moe::decode_matrix_core_passes(*W, T, k) - u);
+    t_dec = bytes / 4.86e6 + extra * expert_bytes(W) / 5.99e6 + 0.081 * entries + 12.1;
   } else {
     const double valu = entries * W->hidden * W->inter * 1.45e-7;
     const double mem_d = bytes / 5.9e6;
     t_dec = std::max(mem_d, valu) + 0.5 * std::min(mem_d, valu) + 4.0;
   }
-  const double t_grp = bytes / (W->format == MOE_W_MXFP4 ? 4.0e6 : 5.2e6) + 25.0;
+  const double t_grp = W->format == MOE_W_MXFP4 ? bytes / 5.11e6 + 0.0057 * entries + 42.8
+                                                 : bytes / 5.2e6 + 25.0;
   return t_grp < t_dec ? MOE_PATH_GROUPED : MOE_PATH_DECODE;
 }
 
