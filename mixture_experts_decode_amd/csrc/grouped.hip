@@ -772,7 +772,7 @@ hipError_t gemm_dispatch(const GemmArgs& a0, int bs, hipStream_t s) {
     // whole 128-byte line (128-K stages fetch half lines); measured on the
     // MXFP4 layer, outputs bit for bit the same: B = 128 314 -> 300 us,
     // B = 256 332 -> 311 us.  The down product gained nothing this way.
-    if constexpr (BFMT == W_MXFP4) {
+    if constexpr (GATEUP && BFMT == W_MXFP4) {
       if (a.K % 256 == 0) {
         MOE_GG(32, 256, 1, 4, 4);
         return hipGetLastError();
