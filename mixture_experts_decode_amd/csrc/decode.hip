@@ -93,6 +93,7 @@ struct DownArgs {
   int nxcd;
   uint32_t slots_magic;
   int rpl;          // rows per lane group in the expert-major kernel
+  int sscl;         // expert-major MXFP8: stage each item's scale bytes in LDS
 };
 
 // entry / slots for entry < 2^24 (slots <= 64): exact with a 32-bit reciprocal.
@@ -412,7 +413,7 @@ struct DownRow {
 // Row d of expert e's W_down.  e is uniform, so the expert's weight and scale
 // bases are scalar; only the offset of the lane's row inside the expert (below
 // 2^31 bytes, checked at launch) is per lane, in 32-bit arithmetic.
-template <int FMT, int LPR, int CPL>
+template <int FMT, int LPR, int CPL, bool SCALES = true>
 __device__ __forceinline__ void load_down_row(DownRow<FMT, CPL>& R, const DownArgs& a, int e,
                                               int d, int gl, bool stream) {
   const uint8_t* base = a.w2 + (size_t)e * a.H * a.row_bytes + (uint32_t)d * (uint32_t)a.row_bytes;
@@ -421,7 +422,9 @@ __device__ __forceinline__ void load_down_row(DownRow<FMT, CPL>& R, const DownAr
   for (int i = 0; i < CPL; ++i) {
     const int c = gl + LPR * i;
     R.w[i] = stream ? load_stream16(base + (uint32_t)c * 16) : load16(base + (uint32_t)c * 16);
-    if constexpr (FMT == W_MXFP8 || FMT == W_MXFP4) {
+    if constexpr (!SCALES) {
+      R.s[i] = 0.0f;   // set by the caller
+    } else if constexpr (FMT == W_MXFP8 || FMT == W_MXFP4) {
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.w2s) + (size_t)e * a.H * scale_len;
       R.s[i] = e8m0_to_f32(sb[(uint32_t)d * scale_len + (FMT == W_MXFP8 ? (c >> 1) : c)]);
     } else if constexpr (FMT == W_FP8B128) {
@@ -522,7 +525,11 @@ MOE_STREAM_KERNEL((h_regs<FMT, CPL, HBF16>() > 48 || CPL >= 12) ? 2 : 4) void do
 // chunk's partial sum is still a fresh dot2 chain over the same pairs in the
 // same order, multiplied into the accumulator by the chunk's scale, then the
 // same lane reduction: y keeps the bits of the other two down kernels.  Per
-// entry only the dot products remain.
+// entry only the dot products remain.  With SSCL (MXFP8 rows, when the host
+// finds the item's scale bytes whole and 16-byte aligned) the item's rows are
+// consecutive rows of W_down, so their E8M0 scales are one run of
+// ND*RPL*I/32 bytes: one 16-byte load per lane brings the run into the
+// wavefront's LDS slice, in place of one byte load per row and chunk.
 template <int LPR>
 __device__ __forceinline__ float lane_group_sum(float acc) {
   if constexpr (LPR == 32) return half32_sum(acc);
@@ -531,11 +538,15 @@ __device__ __forceinline__ float lane_group_sum(float acc) {
   else return group4_sum(acc);
 }
 
-template <int FMT, int LPR, int CPL, int RPL>
+constexpr int kPreScaleBytes = 1024;   // per wavefront: a 16-byte load per lane
+
+template <int FMT, int LPR, int CPL, int RPL, bool SSCL>
 MOE_STREAM_KERNEL(RPL * CPL >= 8 ? 3 : 4) void down_expert_pre_kernel(const DownArgs a) {
   static_assert(FMT == W_MXFP8 || FMT == W_FP8B128, "E4M3 rows");
+  static_assert(!SSCL || FMT == W_MXFP8, "staged E8M0 scales");
   __shared__ int s_ids[kDecodeMaxEntries];
   __shared__ uint32_t s_mask[kMaskWords];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[SSCL ? kWavesPerBlock * kPreScaleBytes : 16];
   constexpr int ND = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = lane / LPR, gl = lane % LPR;
@@ -545,11 +556,21 @@ MOE_STREAM_KERNEL(RPL * CPL >= 8 ? 3 : 4) void down_expert_pre_kernel(const Down
   float* out = reinterpret_cast<float*>(a.y);
   for (int it = blockIdx.x * kWavesPerBlock + wave_in_block(); it < n_items; it += n_waves) {
     const int e = select_rank(s_mask, a.n_words, it / a.n_dgroups);
-    const int d0 = (it % a.n_dgroups) * ND * RPL + grp;
+    const int row0 = (it % a.n_dgroups) * ND * RPL;
+    const int d0 = row0 + grp;
     DownRow<FMT, CPL> raw[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      load_down_row<FMT, LPR, CPL>(raw[r], a, e, min(d0 + r * ND, a.H - 1), gl, true);
+      load_down_row<FMT, LPR, CPL, !SSCL>(raw[r], a, e, min(d0 + r * ND, a.H - 1), gl, true);
+    // SSCL: the host checked that H is a multiple of ND*RPL (no partial
+    // item), that the run is a multiple of 16 bytes and at most
+    // kPreScaleBytes, and that every run starts 16-byte aligned
+    const int scale_len = a.I >> 5;
+    const bool s_lane = SSCL && lane * 16 < ND * RPL * scale_len;
+    u32x4 sv = {0u, 0u, 0u, 0u};
+    if (s_lane)
+      sv = load16(reinterpret_cast<const uint8_t*>(a.w2s) + ((size_t)e * a.H + row0) * scale_len +
+                  lane * 16);
     // wb[r][i][2d], [2d + 1]: the two BF16 pairs of byte pairs 0-1 and 2-3 of dword d
     uint32_t wb[RPL][CPL][8];
 #pragma unroll
@@ -561,6 +582,16 @@ MOE_STREAM_KERNEL(RPL * CPL >= 8 ? 3 : 4) void down_expert_pre_kernel(const Down
           wb[r][i][2 * d] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<false>(raw[r].w[i][d]));
           wb[r][i][2 * d + 1] = __builtin_bit_cast(uint32_t, fp8x2_to_bf16x2<true>(raw[r].w[i][d]));
         }
+    if constexpr (SSCL) {
+      uint8_t* sl = s_scl + wave_in_block() * kPreScaleBytes;
+      if (s_lane) *reinterpret_cast<u32x4*>(sl + lane * 16) = sv;
+      // the same wavefront wrote the slice: its LDS accesses stay in order
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+          raw[r].s[i] = e8m0_to_f32(sl[(grp + r * ND) * scale_len + ((gl + LPR * i) >> 1)]);
+    }
     PairIter pi;
     pairs_begin(pi, s_ids, a.n_entries, e);
     for (int pe = pairs_next(pi, s_ids, a.n_entries, e); pe >= 0;
@@ -1141,13 +1172,20 @@ hipError_t down_launch(const DownArgs& a, int variant, int ybf16, int blocks, hi
   // the kernel that converts each item's rows once.
   if constexpr ((FMT == W_MXFP8 || FMT == W_FP8B128) && HBF16 && CPL <= 4) {
     if (expert_major && (a.rpl == 4 || a.rpl == 2)) {
+      constexpr bool kCanStage = FMT == W_MXFP8;
       if constexpr (CPL <= 3) {
         if (a.rpl == 4) {
-          hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 4>), g, b, 0, s, a);
+          if (kCanStage && a.sscl)
+            hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 4, kCanStage>), g, b, 0, s, a);
+          else
+            hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 4, false>), g, b, 0, s, a);
           return hipGetLastError();
         }
       }
-      hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 2>), g, b, 0, s, a);
+      if (kCanStage && a.sscl)
+        hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 2, kCanStage>), g, b, 0, s, a);
+      else
+        hipLaunchKernelGGL((down_expert_pre_kernel<FMT, LPR, CPL, 2, false>), g, b, 0, s, a);
       return hipGetLastError();
     }
   }
@@ -1364,6 +1402,13 @@ hipError_t plan_down(const moe_weights& W, const void* h, int h_dtype, const int
   const int rpl_max = a.cpl <= 3 ? 4 : a.cpl <= 4 ? 2 : 1;
   a.rpl = em ? std::min(rpl_fit, rpl_max) : 1;
   a.n_dgroups = (W.hidden + nd * a.rpl - 1) / (nd * a.rpl);
+  {
+    // an item's rows' E8M0 scales as one 16-byte-aligned run (see
+    // down_expert_pre_kernel)
+    const long long run = (long long)nd * a.rpl * (W.inter / 32);
+    a.sscl = W.format == W_MXFP8 && em && W.hidden % (nd * a.rpl) == 0 && run % 16 == 0 &&
+             run <= 1024 && (reinterpret_cast<uintptr_t>(W.w2_scale) & 15) == 0;
+  }
   const int n_exp = W.num_experts + W.num_shared;
   a.n_words = (n_exp + 31) / 32;
   a.nxcd = device_num_xcds();

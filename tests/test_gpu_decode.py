@@ -24,6 +24,8 @@ SMALL = {
     "mxfp8": W.QWEN3_DECODE_MXFP8.replace(num_experts=16, tag=21),
     "mxfp4": W.MXFP4_SWEEP.replace(num_experts=16, tag=22),
     "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=12, tag=23),
+    # MXFP8 rows spanning 32 lanes (I = 1536): the other conversion-once shape
+    "mxfp8_i1536": W.PREFILL_ZIPF_MXFP8.replace(num_experts=16, tag=25),
 }
 
 
@@ -320,3 +322,28 @@ def test_mx4_matrix_core_expert_count_not_a_multiple_of_64(lib):
     scale = np.sqrt(np.mean(h_ref ** 2))
     assert np.max(np.abs(to_f64(h) - h_ref)) <= 2e-4 * scale + 1e-6
     assert_layer_close(to_f64(y), y_ref)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp8_i1536"])
+def test_down_scale_staging_fallback_bitwise(lib, fmt):
+    """The conversion-once expert-major down stages each item's E8M0 scales in
+    LDS when the scale array is 16-byte aligned; with the scales one byte off
+    alignment it loads them byte by byte instead.  Both give the same bits,
+    and the same bits as token-major."""
+    cfg = SMALL[fmt]
+    x, ids, w = inputs(cfg, 24)
+    Wd = device_weights(cfg)
+    w13, w13s, w2, w2s = Wd.tensors
+    buf = torch.empty(w2s.numel() + 16, dtype=torch.uint8, device="cuda")
+    mis = buf[1:1 + w2s.numel()].view(w2s.shape)
+    mis.copy_(w2s)
+    assert mis.data_ptr() % 16 == 1
+    Wm = lib.Weights(cfg.fmt, cfg.hidden, cfg.inter, cfg.num_experts, cfg.num_shared,
+                     w13, w13s, w2, mis)
+    idd, wd = device_routing(ids, w)
+    h = lib.gate_up(Wd, to_device_x(cfg, x), idd, h_dtype="bf16")
+    y_staged = lib.down(Wd, h, idd, wd, variant="expert")
+    y_bytes = lib.down(Wm, h, idd, wd, variant="expert")
+    y_tok = lib.down(Wd, h, idd, wd, variant="token")
+    torch.cuda.synchronize()
+    assert torch.equal(y_staged, y_bytes) and torch.equal(y_staged, y_tok)
