@@ -74,6 +74,7 @@ struct GateUpArgs {
   int n_words;      // 32-bit words of the touched-expert mask
   int n_entries;    // T * slots
   uint32_t slots_magic;  // ceil(2^32 / slots): entry / slots by a multiply-high
+  int sscl;         // MXFP8 neuron pairs: the rows' scales as one dword per lane
 };
 
 struct DownArgs {
@@ -260,10 +261,33 @@ __device__ __forceinline__ void chunk_to_bf16(const u32x4 q, uint32_t* out, floa
 template <int FMT, bool PRE>
 constexpr bool scale_folded() { return PRE && (FMT == W_MXFP8 || FMT == W_MXFP4); }
 
+// For MXFP8 neuron pairs (rows of MCH <= 2 whole 64-lane passes) the four
+// rows' E8M0 scales are two runs of 2 * H/32 bytes, the gate rows n0, n0 + 1
+// and the up rows n0, n0 + 1: 32 * MCH dwords.  In the DW instantiation (the
+// host's a.sscl: I even, so n0 + 1 < I, and the scales 4-byte aligned) each
+// lane loads one dword of them, ahead of the rows, and every lane takes its
+// chunks' scale bytes from the lanes holding them (ds_bpermute), in place of
+// a byte load per row and chunk.  Same scale values, same bits.
+template <int FMT, int NR, int MCH, bool GUARD>
+constexpr bool gate_scales_by_dword() {
+  return FMT == W_MXFP8 && NR == 2 && MCH <= 2 && !GUARD;
+}
+
 // GUARD: the row has fewer than 64*MCH chunks, lanes past the end hold zeros.
-template <int FMT, int NR, int MCH, bool PRE, bool GUARD>
+template <int FMT, int NR, int MCH, bool PRE, bool GUARD, bool DW>
 __device__ __forceinline__ void load_gate_rows(GateRows<FMT, NR, MCH, PRE>& R,
                                                const GateUpArgs& a, int e, int n0, int lane) {
+  static_assert(!DW || gate_scales_by_dword<FMT, NR, MCH, GUARD>(), "dword scale shape");
+  constexpr int kRun = 16 * MCH;                  // dwords of two rows' scales
+  const int srow = a.H >> 5;                      // scale bytes per row
+  uint32_t sdw = 0;
+  if constexpr (DW) {
+    if (lane < 2 * kRun) {
+      const int p = lane / kRun, k = lane - p * kRun;
+      sdw = reinterpret_cast<const uint32_t*>(
+          reinterpret_cast<const uint8_t*>(a.w13s) + (((long long)e * 2 + p) * a.I + n0) * srow)[k];
+    }
+  }
   u32x4 raw[2 * NR][MCH];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -278,8 +302,9 @@ __device__ __forceinline__ void load_gate_rows(GateRows<FMT, NR, MCH, PRE>& R,
         const int c = lane + m * kWave;
         if (!GUARD || c < a.chunks) {
           raw[p * NR + rr][m] = load_stream16(base + (size_t)c * 16);
-          R.s[p * NR + rr][m] = chunk_scale<FMT>(
-              a.w13s, row, c, FMT == W_FP8B128 ? (a.H >> 7) : (a.H >> 5), tile_row);
+          if constexpr (!DW)
+            R.s[p * NR + rr][m] = chunk_scale<FMT>(
+                a.w13s, row, c, FMT == W_FP8B128 ? (a.H >> 7) : (a.H >> 5), tile_row);
         } else {
           raw[p * NR + rr][m] = u32x4{0, 0, 0, 0};
           R.s[p * NR + rr][m] = 0.f;
@@ -291,6 +316,13 @@ __device__ __forceinline__ void load_gate_rows(GateRows<FMT, NR, MCH, PRE>& R,
   for (int q = 0; q < 2 * NR; ++q)
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
+      if constexpr (DW) {
+        // chunk lane + 64 m of row q uses the row's scale byte (lane + 64 m) / 2;
+        // row q starts q * srow bytes into the two runs, and lane i holds dword i
+        const int off = q * srow + ((lane + m * kWave) >> 1);
+        const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((off >> 2) << 2, (int)sdw);
+        R.s[q][m] = e8m0_to_f32((v >> (8 * (off & 3))) & 0xffu);
+      }
       if constexpr (PRE) {
         chunk_to_bf16<FMT>(raw[q][m], R.w[q][m], scale_folded<FMT, PRE>() ? R.s[q][m] : 1.0f);
       } else {
@@ -371,7 +403,7 @@ __device__ __forceinline__ void gate_up_pair(GateRows<FMT, NR, MCH, PRE>& R, con
   }
 }
 
-template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD>
+template <int FMT, int NR, int MCH, bool PRE, bool XF32, bool HBF16, bool GUARD, bool DW>
 MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs a) {
   __shared__ int s_ids[kDecodeMaxEntries];
   __shared__ uint32_t s_mask[kMaskWords];
@@ -390,7 +422,7 @@ MOE_STREAM_KERNEL(MCH >= 7 ? 2 : 4) void gate_up_decode_kernel(const GateUpArgs 
     XChunk<FMT, XF32> xc[MCH];
     load_token_x<FMT, MCH, XF32, GUARD>(xc, a, pe, lane);
     GateRows<FMT, NR, MCH, PRE> rows;
-    load_gate_rows<FMT, NR, MCH, PRE, GUARD>(rows, a, e, n0, lane);
+    load_gate_rows<FMT, NR, MCH, PRE, GUARD, DW>(rows, a, e, n0, lane);
     while (true) {
       gate_up_pair<FMT, NR, MCH, PRE, XF32, HBF16, GUARD>(rows, a, xc, pe, n0, lane);
       pe = pairs_next(pi, s_ids, a.n_entries, e);
@@ -1121,10 +1153,18 @@ hipError_t gate_up_mch(const GateUpArgs& a, int mch, bool guard, int blocks, hip
   dim3 g(blocks), b(kBlock);
 #define MOE_GU(M, G)                                                                         \
   do {                                                                                       \
-    if constexpr (gate_up_shape_ok<NR, M, PRE>())                                            \
-      hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G>), g, b, 0, s, a); \
-    else                                                                                     \
+    if constexpr (!gate_up_shape_ok<NR, M, PRE>())                                           \
       return hipErrorNotSupported;                                                           \
+    else if constexpr (gate_scales_by_dword<FMT, NR, M, G>()) {                              \
+      if (a.sscl)                                                                            \
+        hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G, true>), g, b, \
+                           0, s, a);                                                         \
+      else                                                                                   \
+        hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G, false>), g, \
+                           b, 0, s, a);                                                      \
+    } else                                                                                   \
+      hipLaunchKernelGGL((gate_up_decode_kernel<FMT, NR, M, PRE, XF32, HBF16, G, false>), g, b, 0, \
+                         s, a);                                                              \
   } while (0)
   if (!guard) {
     switch (mch) {
@@ -1305,6 +1345,9 @@ hipError_t plan_gate_up(const moe_weights& W, const void* x, const int32_t* ids,
   p.pre = W.format != W_F32 && p.mch <= 4 && 2 * p.nr * p.mch * elems / 2 <= 64;
   a.slots_magic = (uint32_t)(((1ull << 32) + a.slots - 1) / a.slots);
   a.n_groups = (W.inter + p.nr - 1) / p.nr;
+  // neuron pairs never straddle the end of I, and the scales load as dwords
+  a.sscl = W.format == W_MXFP8 && W.inter % 2 == 0 &&
+           (reinterpret_cast<uintptr_t>(W.w13_scale) & 3) == 0;
   const long long max_items = (long long)std::min(n_exp, a.n_entries) * a.n_groups;
   const long long want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
   p.blocks = (int)std::max<long long>(1, std::min<long long>(want, device_num_cus() * 16LL));

@@ -347,3 +347,25 @@ def test_down_scale_staging_fallback_bitwise(lib, fmt):
     y_tok = lib.down(Wd, h, idd, wd, variant="token")
     torch.cuda.synchronize()
     assert torch.equal(y_staged, y_bytes) and torch.equal(y_staged, y_tok)
+
+
+@pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
+def test_gate_up_scale_dwords_fallback_bitwise(lib, h_dtype):
+    """MXFP8 gate_up reads a neuron pair's scales as one dword per lane when
+    the scale array is 4-byte aligned, byte by byte otherwise: same bits."""
+    cfg = SMALL["mxfp8"]
+    x, ids, w = inputs(cfg, 13)
+    Wd = device_weights(cfg)
+    w13, w13s, w2, w2s = Wd.tensors
+    buf = torch.empty(w13s.numel() + 16, dtype=torch.uint8, device="cuda")
+    mis = buf[1:1 + w13s.numel()].view(w13s.shape)
+    mis.copy_(w13s)
+    assert mis.data_ptr() % 4 != 0
+    Wm = lib.Weights(cfg.fmt, cfg.hidden, cfg.inter, cfg.num_experts, cfg.num_shared,
+                     w13, mis, w2, w2s)
+    xd = to_device_x(cfg, x)
+    idd, _ = device_routing(ids, w)
+    h_dw = lib.gate_up(Wd, xd, idd, h_dtype=h_dtype)
+    h_bytes = lib.gate_up(Wm, xd, idd, h_dtype=h_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(h_dw, h_bytes)
