@@ -25,8 +25,12 @@ MODE = {"decode": "none", "grouped": "mxfp8"}
 # (workload, B, routing kind, tokens compared: None = every token, else how many)
 CASES = [
     ("qwen3_decode_mxfp8", 32, None, None),
+    # just past the decode down's expert-major switch (112 routed entries)
+    ("qwen3_decode_mxfp8", 14, None, None),
     ("qwen3_decode_mxfp8", 64, None, 8),
     ("deepseek_v3_fp8_blk128", 1, None, None),
+    # 18 routed entries: expert-major down on 32-lane FP8-128 rows
+    ("deepseek_v3_fp8_blk128", 2, None, None),
     ("deepseek_v3_fp8_blk128", 64, None, 3),
     ("mxfp4_sweep", 8, "uniform", None),
     ("mxfp4_sweep", 8, "zipf", None),
