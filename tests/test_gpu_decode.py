@@ -26,6 +26,8 @@ SMALL = {
     "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=12, tag=23),
     # MXFP8 rows spanning 32 lanes (I = 1536): the other conversion-once shape
     "mxfp8_i1536": W.PREFILL_ZIPF_MXFP8.replace(num_experts=16, tag=25),
+    # H = 1024: gate_up rows of one chunk per lane (its scale dwords from 16 lanes)
+    "mxfp8_h1024": W.QWEN3_DECODE_MXFP8.replace(hidden=1024, num_experts=16, tag=26),
 }
 
 
@@ -349,11 +351,12 @@ def test_down_scale_staging_fallback_bitwise(lib, fmt):
     assert torch.equal(y_staged, y_bytes) and torch.equal(y_staged, y_tok)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp8_h1024"])
 @pytest.mark.parametrize("h_dtype", ["f32", "bf16"])
-def test_gate_up_scale_dwords_fallback_bitwise(lib, h_dtype):
+def test_gate_up_scale_dwords_fallback_bitwise(lib, fmt, h_dtype):
     """MXFP8 gate_up reads a neuron pair's scales as one dword per lane when
     the scale array is 4-byte aligned, byte by byte otherwise: same bits."""
-    cfg = SMALL["mxfp8"]
+    cfg = SMALL[fmt]
     x, ids, w = inputs(cfg, 13)
     Wd = device_weights(cfg)
     w13, w13s, w2, w2s = Wd.tensors
