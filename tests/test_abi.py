@@ -251,3 +251,47 @@ def test_noalloc_entry_point_host_checks(lib):
     assert lib.moe_layer_noalloc(ctypes.byref(w), None, 1, None, None, 0, 8, None, 0, 0, 0,
                                  ctypes.byref(chosen), None) == moe.OK
     assert chosen.value == 1
+
+
+def test_path_choice_and_workspace_rules_over_random_shapes(lib):
+    """Host rules over a seeded spread of layer shapes (no GPU): the regime
+    choice is monotone in the batch, the decode workspace is h plus, exactly
+    when the down product runs expert-major, the FP32 slot outputs, and every
+    shape AUTO sends to the decode path (quantised weights) is one the decode
+    entry points accept."""
+    import numpy as np
+    moe = __import__("mixture_experts_decode_amd")
+    DEC, GRP = 1, 2
+    rng = np.random.default_rng(2024)
+    align = lambda n: (n + 255) // 256 * 256
+    for _ in range(120):
+        fmt = int(rng.choice([0, 1, 2, 3]))
+        hidden = int(rng.choice([512, 1024, 2048, 4096, 7168]))
+        inter = int(rng.choice([256, 512, 768, 1024, 1536, 2048]))
+        e = int(rng.choice([8, 16, 64, 128, 256]))
+        s = int(rng.integers(0, 2))
+        k = int(rng.choice([1, 2, 4, 6, 8]))
+        if k > e:
+            continue
+        w = _weights(moe, hidden=hidden, inter=inter, num_experts=e, num_shared=s, format=fmt)
+        picks = [lib.moe_choose_path(ctypes.byref(w), t, k) for t in range(0, 260, 3)]
+        if GRP in picks:
+            first = picks.index(GRP)
+            assert all(p == DEC for p in picks[:first]) and all(p == GRP for p in picks[first:])
+        h_el = 4 if fmt == 0 else 2
+        dummy = ctypes.c_void_p(4096)
+        for t in (1, 2, 7, 13, 14, 32, 100):
+            if lib.moe_choose_path(ctypes.byref(w), t, k) != DEC:
+                continue
+            ws = lib.moe_layer_workspace_bytes(ctypes.byref(w), t, k, DEC, 0)
+            h_bytes = align(t * (k + s) * inter * h_el)
+            slot = align(t * (k + s) * hidden * 4)
+            assert ws in (h_bytes, h_bytes + slot), (fmt, hidden, inter, e, s, k, t, ws)
+            # every host check passes: with no GPU here the call can only fail
+            # at its first launch (MOE_ERR_HIP), never with a refusal -- except
+            # FP32 weights, which have no grouped path to fall back to, so AUTO
+            # names the decode path even for rows it cannot take
+            st = lib.moe_layer(ctypes.byref(w), dummy, 0 if fmt == 0 else 1, dummy, dummy, t, k,
+                               dummy, 0, DEC, 0, dummy, ws, None, None)
+            ok = (moe.ERR_HIP, moe.ERR_UNSUPPORTED) if fmt == 0 else (moe.ERR_HIP,)
+            assert st in ok, (fmt, hidden, inter, e, s, k, t, st)
