@@ -124,7 +124,8 @@ int32_t moe_decode_max_entries(void);
  * once and its reduction order does not depend on the batch.
  *   x        device, [T][H], x_dtype (MOE_DT_F32 only with MOE_W_F32 weights)
  *   topk_ids device, [T][k] int32
- *   h        device, [T][slots][I], h_dtype
+ *   h        device, [T][slots][I], h_dtype (MOE_W_F32 weights take MOE_DT_F32
+ *            only: MOE_ERR_UNSUPPORTED otherwise, as in moe_down)
  * T == 0 is a no-op.  T * slots must not exceed moe_decode_max_entries().
  */
 moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
@@ -169,7 +170,8 @@ typedef enum {
  * products summed in another FP32 order, so its bits differ from the
  * token-major shape's.  AUTO takes it at every T for such weights, so y still
  * does not depend on the batch.
- *   h            device, [T][slots][I], h_dtype
+ *   h            device, [T][slots][I], h_dtype (MOE_DT_F32 only with
+ *                MOE_W_F32 weights)
  *   topk_ids     device, [T][k] int32; topk_weights device, [T][k] float32
  *   y            device, [T][H], y_dtype
  *   variant      moe_down_variant

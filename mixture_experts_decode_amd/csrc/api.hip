@@ -252,6 +252,8 @@ moe_status moe_gate_up(const moe_weights* W, const void* x, int32_t x_dtype,
   if (T == 0) return MOE_OK;
   if (!x || !h || (k > 0 && !topk_ids) || !aligned16(x)) return MOE_ERR_INVALID_ARG;
   if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
+  // FP32 weights pair with an FP32 h: moe_down takes no BF16 h for them
+  if (h_dtype == MOE_DT_BF16 && W->format == MOE_W_F32) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)T * (k + W->num_shared) > kDecodeMaxEntries) return MOE_ERR_UNSUPPORTED;
   return from_hip(moe::launch_gate_up_decode(*W, x, x_dtype, topk_ids, T, k, h, h_dtype,
                                              as_stream(stream)));

@@ -78,6 +78,11 @@ def test_host_argument_errors(lib):
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 1, dummy, 4096, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
     # f32 activations with quantised weights
     assert lib.moe_gate_up(ctypes.byref(w), dummy, 0, dummy, 4, 8, dummy, 0, None) == moe.ERR_UNSUPPORTED
+    # FP32 weights take an FP32 h in both products (a BF16 h is refused)
+    w32 = _weights(moe, format=0, w13_scale=None, w2_scale=None)
+    assert lib.moe_gate_up(ctypes.byref(w32), dummy, 0, dummy, 4, 8, dummy, 1, None) == moe.ERR_UNSUPPORTED
+    assert lib.moe_down(ctypes.byref(w32), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 1, None, 0,
+                        None) == moe.ERR_UNSUPPORTED
     # misaligned weight pointer, bad format, non-multiple-of-32 hidden
     assert lib.moe_down(ctypes.byref(_weights(moe, w13=17)), dummy, 0, dummy, dummy, 4, 8, dummy, 0,
                         0, None, 0, None) == moe.ERR_INVALID_ARG
