@@ -28,6 +28,9 @@ SMALL = {
     "mxfp8_i1536": W.PREFILL_ZIPF_MXFP8.replace(num_experts=16, tag=25),
     # H = 1024: gate_up rows of one chunk per lane (its scale dwords from 16 lanes)
     "mxfp8_h1024": W.QWEN3_DECODE_MXFP8.replace(hidden=1024, num_experts=16, tag=26),
+    # E2M1 rows off the matrix-core kernel's grid (I not a multiple of 256):
+    # both products run on the vector kernels, rows converted per token
+    "mxfp4_i384": W.MXFP4_SWEEP.replace(inter=384, num_experts=16, tag=27),
 }
 
 
@@ -63,7 +66,7 @@ def test_decode_parity_small(lib, fmt, t):
     assert_layer_close(to_f64(y), y_ref, (fmt, t))
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8_blk128"])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8_blk128", "mxfp4_i384"])
 def test_decode_bf16_intermediate_and_output(lib, fmt):
     cfg = SMALL[fmt]
     x, ids, w, h, y = _run_decode(lib, cfg, 7, h_dtype="bf16", y_dtype="bf16")
@@ -86,7 +89,7 @@ def test_down_alone_on_given_h(lib):
     assert_layer_close(to_f64(y), ref)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8_blk128"])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8_blk128", "mxfp4_i384"])
 def test_batch_invariance_and_determinism(lib, fmt):
     """Each output is produced by one wavefront in a fixed order, so a token's
     h and y do not depend on the rest of the batch and repeat bit for bit
