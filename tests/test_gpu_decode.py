@@ -31,6 +31,13 @@ SMALL = {
     # E2M1 rows off the matrix-core kernel's grid (I not a multiple of 256):
     # both products run on the vector kernels, rows converted per token
     "mxfp4_i384": W.MXFP4_SWEEP.replace(inter=384, num_experts=16, tag=27),
+    # rows that are not whole 64-lane passes of 16-byte chunks: the guarded
+    # gate_up shape in every format (and down rows past the last full group)
+    "mxfp8_h1056": W.QWEN3_DECODE_MXFP8.replace(hidden=1056, num_experts=16, tag=28),
+    "f32_h200": W.TINY_FP32.replace(hidden=200, inter=96, tag=29),
+    "fp8_blk128_h1152": W.DEEPSEEK_V3_FP8_BLK128.replace(hidden=1152, inter=256, num_experts=12,
+                                                        tag=30),
+    "mxfp4_h1088": W.MXFP4_SWEEP.replace(hidden=1088, inter=384, num_experts=16, tag=31),
 }
 
 
@@ -118,7 +125,7 @@ def test_batch_invariance_and_determinism(lib, fmt):
 
 # FP32 weights take an FP32 h only (the library refuses a BF16 one)
 @pytest.mark.parametrize("fmt,h_dtype", [(f, hd) for f in SMALL for hd in ("f32", "bf16")
-                                         if not (f == "f32" and hd == "bf16")])
+                                         if not (SMALL[f].fmt == "f32" and hd == "bf16")])
 def test_down_variants_bitwise_identical(lib, fmt, h_dtype):
     """Token-major and expert-major down give the same bits (same per-slot
     lane groups and reduction tree, slots added in slot order) -- except
