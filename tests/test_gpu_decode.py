@@ -38,6 +38,13 @@ SMALL = {
     "fp8_blk128_h1152": W.DEEPSEEK_V3_FP8_BLK128.replace(hidden=1152, inter=256, num_experts=12,
                                                         tag=30),
     "mxfp4_h1088": W.MXFP4_SWEEP.replace(hidden=1088, inter=384, num_experts=16, tag=31),
+    # long rows: 3, 5 and 8 chunks per lane (the guarded 4- and 8-chunk shapes
+    # and the unguarded 8-chunk one, rows streamed without the BF16 copy)
+    "mxfp8_h3072": W.QWEN3_DECODE_MXFP8.replace(hidden=3072, inter=256, num_experts=16, tag=32),
+    "mxfp8_h5120": W.QWEN3_DECODE_MXFP8.replace(hidden=5120, inter=256, num_experts=16, tag=33),
+    "mxfp8_h8192": W.QWEN3_DECODE_MXFP8.replace(hidden=8192, inter=256, num_experts=16, tag=34),
+    "f32_h2048": W.TINY_FP32.replace(hidden=2048, inter=64, tag=35),
+    "f32_h1536": W.TINY_FP32.replace(hidden=1536, inter=64, tag=36),
 }
 
 
