@@ -19,6 +19,10 @@ SMALL = {
     "mxfp8": W.PREFILL_ZIPF_MXFP8.replace(num_experts=8, tag=31),
     "mxfp4": W.MXFP4_SWEEP.replace(num_experts=8, tag=32),
     "fp8_blk128": W.DEEPSEEK_V3_FP8_BLK128.replace(num_experts=6, tag=33),
+    # E2M1 rows with H not a multiple of 256: the 32-row gate_up tile keeps
+    # 128-K stages (half-line weight slices) instead of 256-K ones, and the
+    # last 512-row down tile is partial
+    "mxfp4_h3968": W.MXFP4_SWEEP.replace(hidden=3968, num_experts=8, tag=34),
 }
 
 
@@ -196,7 +200,7 @@ def _grouped_layer(lib, cfg, t, bs, kind=None):
 
 @pytest.mark.parametrize("fmt,t,bs", [("mxfp8", 40, 64), ("mxfp4", 33, 32), ("fp8_blk128", 21, 32),
                                       ("fp8_blk128", 150, 128), ("mxfp4", 170, 128), ("mxfp8", 1, 32),
-                                      ("mxfp8", 300, 128)])
+                                      ("mxfp8", 300, 128), ("mxfp4_h3968", 33, 32)])
 def test_grouped_layer_small(lib, fmt, t, bs):
     cfg = SMALL[fmt]
     x, ids, w, y = _grouped_layer(lib, cfg, t, bs)
