@@ -25,6 +25,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "mx_quant.h"
 
 namespace moe {
 
@@ -242,7 +243,7 @@ __device__ __forceinline__ void place_range(const AsArgs& a, int* ctr, int lo, i
 // kPrefixBlock threads (up to kFusedWaves wavefronts, each on its own
 // contiguous range), all exchanged through LDS -- one launch, no global
 // scratch.  Same results as the three-launch path.
-__global__ __launch_bounds__(kPrefixBlock) void as_fused_kernel(const AsArgs a) {
+__device__ __forceinline__ void as_fused_body(const AsArgs& a) {
   __shared__ int s_h[kFusedWaves][kMaxExpertsTotal];   // per-wave counts, then bases
   __shared__ int s_off[kMaxExpertsTotal + 1];
   __shared__ int s_cnt[kMaxExpertsTotal];
@@ -277,6 +278,24 @@ __global__ __launch_bounds__(kPrefixBlock) void as_fused_kernel(const AsArgs a) 
   }
 }
 
+__global__ __launch_bounds__(kPrefixBlock) void as_fused_kernel(const AsArgs a) { as_fused_body(a); }
+
+// The layer's grouped front end up to kFusedMaxEntries entries, in one
+// launch: workgroup 0 sorts the entries (as above) while the others quantise
+// the token rows to MXFP8, one wavefront per row.  The two steps do not
+// depend on each other, so the quantisation runs in the sort's shadow; the
+// outputs are those of the two separate calls.
+template <bool XF32>
+__global__ __launch_bounds__(kPrefixBlock) void front_end_kernel(const AsArgs a, const void* x,
+                                                                 int H, uint8_t* xq, uint8_t* xs) {
+  if (blockIdx.x == 0) {
+    as_fused_body(a);
+    return;
+  }
+  const int t = (blockIdx.x - 1) * kFusedWaves + (int)(threadIdx.x >> 6);
+  if (t < a.T) quant_row<XF32>(x, t, H, xq, xs, threadIdx.x & (kWave - 1));
+}
+
 AsArgs make_args(const int32_t* ids, int T, int k, int E, int S, int bs) {
   AsArgs a{};
   a.ids = ids;
@@ -295,6 +314,13 @@ AsArgs make_args(const int32_t* ids, int T, int k, int E, int S, int bs) {
   while ((1 << bits) < a.n_exp) ++bits;
   a.id_bits = bits;
   return a;
+}
+
+// one workgroup: at most kFusedWaves ranges of whole 64-entry chunks
+void set_fused_ranges(AsArgs& a) {
+  const int chunks = std::max(1, (a.n + kWave - 1) / kWave);
+  a.per_wave = (chunks + kFusedWaves - 1) / kFusedWaves * kWave;
+  a.n_waves = std::max(1, (a.n + a.per_wave - 1) / a.per_wave);
 }
 
 }  // namespace
@@ -316,10 +342,7 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int
   a.offsets = offsets;
   a.npp = npp;
   if (a.n <= kFusedMaxEntries) {
-    // one workgroup: at most kFusedWaves ranges of whole 64-entry chunks
-    const int chunks = std::max(1, (a.n + kWave - 1) / kWave);
-    a.per_wave = (chunks + kFusedWaves - 1) / kFusedWaves * kWave;
-    a.n_waves = std::max(1, (a.n + a.per_wave - 1) / a.per_wave);
+    set_fused_ranges(a);
     hipLaunchKernelGGL(as_fused_kernel, dim3(1), dim3(kPrefixBlock), 0, s, a);
     return hipGetLastError();
   }
@@ -333,6 +356,29 @@ hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(as_place_kernel, dim3(blocks), dim3(kAsBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_front_end(const int32_t* ids, int T, int k, int E, int S, int bs,
+                            int32_t* sorted, int32_t* expert_ids, int32_t* offsets, int32_t* npp,
+                            void* ws, const void* x, int x_dtype, int H, uint8_t* xq, uint8_t* xs,
+                            hipStream_t s) {
+  AsArgs a = make_args(ids, T, k, E, S, bs);
+  if (a.n > kFusedMaxEntries || T == 0) {
+    hipError_t err = launch_align_sort(ids, T, k, E, S, bs, sorted, expert_ids, offsets, npp, ws, s);
+    if (err != hipSuccess) return err;
+    return launch_quant_rows(x, x_dtype, T, H, xq, xs, s);
+  }
+  a.sorted = sorted;
+  a.expert_ids = expert_ids;
+  a.offsets = offsets;
+  a.npp = npp;
+  set_fused_ranges(a);
+  const dim3 grid(1 + (T + kFusedWaves - 1) / kFusedWaves), block(kPrefixBlock);
+  if (x_dtype == MOE_DT_F32)
+    hipLaunchKernelGGL(front_end_kernel<true>, grid, block, 0, s, a, x, H, xq, xs);
+  else
+    hipLaunchKernelGGL(front_end_kernel<false>, grid, block, 0, s, a, x, H, xq, xs);
   return hipGetLastError();
 }
 

@@ -478,10 +478,9 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
   uint8_t* hs = reinterpret_cast<uint8_t*>(ws + L.hs);
   uint16_t* so = reinterpret_cast<uint16_t*>(ws + L.slot_out);
-  hipError_t e = moe::launch_align_sort(topk_ids, T, k, W->num_experts, W->num_shared, block_size,
-                                        sorted, eids, offs, npp, ws + L.as_ws, s);
-  if (e != hipSuccess) return from_hip(e);
-  e = moe::launch_quant_rows(x, x_dtype, T, W->hidden, xq, xs, s);
+  hipError_t e = moe::launch_front_end(topk_ids, T, k, W->num_experts, W->num_shared, block_size,
+                                       sorted, eids, offs, npp, ws + L.as_ws, x, x_dtype, W->hidden,
+                                       xq, xs, s);
   if (e != hipSuccess) return from_hip(e);
   e = moe::launch_grouped_gate_up(*W, xq, xs, T, slots, sorted, eids, npp, L.cap, block_size, hq,
                                   hs, s);

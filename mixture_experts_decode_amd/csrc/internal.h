@@ -41,6 +41,13 @@ size_t align_sort_workspace_bytes(int n_entries, int n_experts);
 hipError_t launch_align_sort(const int32_t* ids, int T, int k, int E, int S, int bs,
                              int32_t* sorted, int32_t* expert_ids, int32_t* offsets,
                              int32_t* npp, void* ws, hipStream_t s);
+// moe_layer's grouped front end: the align-sort above and the MXFP8
+// quantisation of the token rows (launch_quant_rows), as one launch up to the
+// single-workgroup sort's entry limit, else the separate launches
+hipError_t launch_front_end(const int32_t* ids, int T, int k, int E, int S, int bs,
+                            int32_t* sorted, int32_t* expert_ids, int32_t* offsets, int32_t* npp,
+                            void* ws, const void* x, int x_dtype, int H, uint8_t* xq, uint8_t* xs,
+                            hipStream_t s);
 
 // grouped.hip
 hipError_t launch_quant_rows(const void* x, int x_dtype, int T, int H, uint8_t* xq, uint8_t* xs,

@@ -268,3 +268,27 @@ def test_layer_auto_matches_the_oracle_mode_of_its_path(lib, t, want):
     mode = "none" if chosen == "decode" else "mxfp8"
     ref = L.moe_layer(x64, ids[sample], w[sample], act_quant=mode, **oracle_kw(cfg))
     assert_layer_close(to_f64(y)[sample], ref, (t, chosen))
+
+
+@pytest.mark.parametrize("t,bs", [(1, 32), (40, 64), (1100, 128)])
+def test_layer_front_end_matches_the_separate_calls(lib, t, bs):
+    """moe_layer's grouped front end (the sort and the token quantisation in
+    one launch up to 8192 entries, separate launches beyond: 1100 tokens x 8
+    slots here) gives the bits of the separate entry points."""
+    cfg = SMALL["mxfp8"]
+    x, ids, w = inputs(cfg, t)
+    Wd = device_weights(cfg)
+    xd = to_device_x(cfg, x)
+    idd, wd = device_routing(ids, w)
+    y, chosen = lib.layer(Wd, xd, idd, wd, path="grouped", block=bs)
+    k, S = cfg.top_k, cfg.num_shared
+    srt = lib.align_sort(idd, cfg.num_experts, S, bs)
+    xq, xs = lib.quant_rows(xd)
+    cap = lib.align_sort_capacity(t, k, cfg.num_experts, S, bs)
+    hq, hs = lib.grouped_gate_up(Wd, xq, xs, t, k, srt["sorted_token_ids"], srt["expert_ids"],
+                                 srt["num_tokens_post_padded"], cap, bs)
+    so = lib.grouped_down(Wd, hq, hs, srt["sorted_token_ids"], srt["expert_ids"],
+                          srt["num_tokens_post_padded"], cap, bs, wd, t, k)
+    y_sep = lib.combine(so, t, k + S)
+    torch.cuda.synchronize()
+    assert chosen == "grouped" and torch.equal(y, y_sep)
