@@ -252,7 +252,12 @@ def main():
 
         def median_replay_us(graph, launches, n=5):
             """µs per launch: the median over n replays of a graph of
-            `launches` launches, each timed alone on the launch stream."""
+            `launches` launches, each timed alone on the launch stream, after
+            0.2 s of untimed replays (the steady state, as for the layer)."""
+            t_w = time.perf_counter()
+            while time.perf_counter() - t_w < 0.2:
+                graph.replay()
+                torch.cuda.synchronize()
             t = []
             for _ in range(n):
                 s0.record(stream)

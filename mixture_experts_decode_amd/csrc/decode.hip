@@ -1306,7 +1306,7 @@ struct GateUpPlan {
 struct DownPlan {
   DownArgs a;
   int lpr, blocks;
-  int variant;     // kDownTokenMajor, kDownRowBlock or kDownExpertMajor
+  int variant;     // kDownTokenMajor or kDownExpertMajor
 };
 
 hipError_t plan_gate_up(const moe_weights& W, const void* x, const int32_t* ids, int T, int k,
