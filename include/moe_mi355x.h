@@ -370,6 +370,9 @@ size_t moe_layer_workspace_bytes(const moe_weights* W, int32_t T, int32_t k,
 
 /*
  * moe_layer: y = the routed-expert FFN of the layer for T tokens.
+ *   x           device, [T][H], x_dtype: MOE_DT_BF16, or MOE_DT_F32 with
+ *               MOE_W_F32 weights only (MOE_ERR_UNSUPPORTED otherwise, on
+ *               either path, before any launch)
  *   path        MOE_PATH_AUTO / DECODE / GROUPED
  *   block_size  grouped path M block (32, 64 or 128), or 0: the library picks
  *               by the expected entries per expert (32 up to 48, 64 up to

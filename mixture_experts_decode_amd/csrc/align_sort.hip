@@ -364,7 +364,7 @@ hipError_t launch_front_end(const int32_t* ids, int T, int k, int E, int S, int 
                             void* ws, const void* x, int x_dtype, int H, uint8_t* xq, uint8_t* xs,
                             hipStream_t s) {
   AsArgs a = make_args(ids, T, k, E, S, bs);
-  if (a.n > kFusedMaxEntries || T == 0) {
+  if (a.n > kFusedMaxEntries || T == 0 || x_dtype == MOE_DT_F32) {
     hipError_t err = launch_align_sort(ids, T, k, E, S, bs, sorted, expert_ids, offsets, npp, ws, s);
     if (err != hipSuccess) return err;
     return launch_quant_rows(x, x_dtype, T, H, xq, xs, s);
@@ -375,10 +375,7 @@ hipError_t launch_front_end(const int32_t* ids, int T, int k, int E, int S, int 
   a.npp = npp;
   set_fused_ranges(a);
   const dim3 grid(1 + (T + kFusedWaves - 1) / kFusedWaves), block(kPrefixBlock);
-  if (x_dtype == MOE_DT_F32)
-    hipLaunchKernelGGL(front_end_kernel<true>, grid, block, 0, s, a, x, H, xq, xs);
-  else
-    hipLaunchKernelGGL(front_end_kernel<false>, grid, block, 0, s, a, x, H, xq, xs);
+  hipLaunchKernelGGL(front_end_kernel<false>, grid, block, 0, s, a, x, H, xq, xs);
   return hipGetLastError();
 }
 

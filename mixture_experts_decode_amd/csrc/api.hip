@@ -443,12 +443,13 @@ moe_status moe_layer(const moe_weights* W, const void* x, int32_t x_dtype,
   if (T == 0) return MOE_OK;
   if (!x || !y || (k > 0 && (!topk_ids || !topk_weights)) || !workspace)
     return MOE_ERR_INVALID_ARG;
+  // FP32 activations go with FP32 weights only, on either path
+  if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   const int32_t slots = k + W->num_shared;
   if (path == MOE_PATH_DECODE) {
     if (workspace_bytes < decode_workspace(W, T, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace) || !aligned16(x)) return MOE_ERR_INVALID_ARG;
-    if (x_dtype == MOE_DT_F32 && W->format != MOE_W_F32) return MOE_ERR_UNSUPPORTED;
     const int32_t hdt = decode_h_dtype(W);
     // every shape limit of both kernels is checked before the first launch
     if (moe::decode_supported(*W, T, k, hdt) != hipSuccess) return MOE_ERR_UNSUPPORTED;

@@ -120,6 +120,10 @@ def test_host_argument_errors(lib):
                               None) == moe.ERR_WORKSPACE_TOO_SMALL
     assert lib.moe_align_sort(dummy, 4, 8, 2000, 0, 64, dummy, dummy, dummy, dummy, dummy, 1 << 20,
                               None) == moe.ERR_UNSUPPORTED
+    # layer: FP32 activations with quantised weights, on either path
+    for path in (1, 2):
+        assert lib.moe_layer(ctypes.byref(w), dummy, 0, dummy, dummy, 4, 8, dummy, 0, path, 32, dummy,
+                             1 << 30, None, None) == moe.ERR_UNSUPPORTED
     # layer: workspace too small, bad path, grouped with a bad block size
     assert lib.moe_layer(ctypes.byref(w), dummy, 1, dummy, dummy, 4, 8, dummy, 0, 1, 64, dummy, 16,
                          None, None) == moe.ERR_WORKSPACE_TOO_SMALL
